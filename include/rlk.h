@@ -1,0 +1,174 @@
+/*
+ * rlk.h — C ABI of the fused, deterministic selected-token log-probability
+ * operator ("linear_logp") for AMD Instinct MI355X (gfx950).
+ *
+ * The operator ("Announcing RL-Kernel for vime", sections "Key Capabilities"
+ * and "Why the Fused Path Wins"): from bf16 hidden states h [T,H], the bf16
+ * LM-head weight W [V,H] and int32 target ids y [T], compute per row
+ *
+ *     logp[t] = z[t, y_t] - log(sum_v exp(z[t, v])),   z = h W^T,
+ *
+ * without ever storing the [T, V] logits, plus the deterministic gradient of
+ * sum_t g_t * logp_t with respect to h and W.
+ *
+ * Numerical contract (version RLK_CONTRACT_VERSION).  The pages require the
+ * partitioning, merge order, precision, rounding points and primitives to be
+ * fixed ("vLLM RL-Kernel v0.1.0: Bitwise Train-Rollout Consistency on ROCm",
+ * section "The Numerical Execution Contract") but publish no constants; the
+ * ones below are this library's own:
+ *   - logits: bf16 x bf16 products accumulated in fp32 by one
+ *     v_mfma_f32_32x32x16_bf16 chain per logit, k ascending in steps of 16;
+ *   - the vocabulary is split into 32 contiguous splits of width
+ *     S = ceil(V_global / 32); each split into chunks of 128 columns anchored
+ *     at the split start (the last chunk may be short);
+ *   - chunk statistics (m, s): m = max of the chunk's logits, s = sum of
+ *     exp(z - m) in a fixed lane order; chunks of a split are folded left to
+ *     right with the operator  (ma,sa) + (mb,sb) = (m, sa*e(ma-m) + sb*e(mb-m)),
+ *     m = max(ma,mb); splits are merged with a balanced binary tree;
+ *   - exp(x) = exp2(x * log2(e)) and log(x) = log2(x) * ln(2) on the
+ *     hardware exp2/log2, every operation rounded separately (no FMA
+ *     contraction);
+ *   - logp = (z_t - m) - log(s), lse = m + log(s), both fp32.
+ * Consequences: a row's results depend only on that row (batch- and
+ * order-invariant), repeated runs are bit-identical, and merging the partials
+ * of equal, aligned power-of-two blocks of splits reproduces the unsharded
+ * result bit for bit.
+ *
+ * Conventions for every call below:
+ *   - tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *     16-byte aligned; the caller owns every buffer and the library keeps no
+ *     pointer after the call returns;
+ *   - `stream` is a hipStream_t (NULL = the default stream); calls only
+ *     enqueue work on it, never synchronise and never allocate device memory;
+ *   - scratch space is the caller's `ws` buffer of at least
+ *     rlk_workspace_bytes(...) bytes, used only until the enqueued work ends;
+ *   - outputs are overwritten, never accumulated;
+ *   - host-detectable errors return a status and enqueue nothing; data errors
+ *     the host cannot see (a target outside [0,V) that is not ignore_index,
+ *     or no part owning an active target) give NaN in that row's logp;
+ *   - T == 0 returns RLK_OK without launching anything.
+ */
+#ifndef RLK_H_
+#define RLK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLK_CONTRACT_VERSION 1
+#define RLK_NSPLIT 32
+#define RLK_CHUNK 128
+
+typedef int32_t rlk_status;
+enum {
+  RLK_OK = 0,
+  RLK_ERR_NULL_ARG = 1,              /* a required pointer is NULL */
+  RLK_ERR_BAD_SHAPE = 2,             /* T<0, H<=0 or H%64!=0, V<=0, sizes too large */
+  RLK_ERR_BAD_ALIGNMENT = 3,         /* a tensor pointer is not 16-byte aligned */
+  RLK_ERR_UNALIGNED_VOCAB_RANGE = 4, /* a vocab range that is not an aligned block of splits */
+  RLK_ERR_WORKSPACE_TOO_SMALL = 5,   /* ws_bytes < rlk_workspace_bytes(...) */
+  RLK_ERR_HIP = 6,                   /* a HIP runtime call or kernel launch failed */
+  RLK_ERR_UNSUPPORTED_DEVICE = 7,    /* the current device is not gfx950 */
+  RLK_ERR_BAD_ARG = 8                /* another invalid argument (e.g. n_parts < 1) */
+};
+
+/* Per-row statistics of one vocabulary range (16 bytes).
+ * m = max logit over the range, s = sum of exp(z - m) over the range,
+ * z_target = the target's logit when owned == 1 (target inside the range),
+ * else 0.  Rows whose target is ignore_index hold {-inf, 0, 0, 0}.
+ * "Why the Fused Path Wins" (third reason): ranks combine only these
+ * statistics to obtain the global selected log-probability. */
+typedef struct {
+  float m;
+  float s;
+  float z_target;
+  uint32_t owned;
+} rlk_lse_partial_t;
+
+enum { RLK_OP_FWD = 0, RLK_OP_BWD = 1, RLK_OP_PARTIAL = 2 };
+
+/* Identifier of the numerical contract above; results with equal version
+ * and equal inputs are bit-identical. */
+int32_t rlk_contract_version(void);
+
+/* Static text for a status code. */
+const char* rlk_status_string(rlk_status s);
+
+/* Detail of the last error on the calling thread (e.g. the HIP error text);
+ * empty string when none. */
+const char* rlk_last_error_message(void);
+
+/* Workspace bytes needed by `op` (RLK_OP_*) for T rows, hidden size H and a
+ * vocabulary of V rows (for RLK_OP_PARTIAL: V = V_global, the size of the
+ * whole vocabulary).  Returns 0 for invalid arguments. */
+size_t rlk_workspace_bytes(int32_t op, int64_t T, int64_t H, int64_t V);
+
+/* Forward ("Announcing RL-Kernel for vime", "Key Capabilities": the
+ * log-softmax of hidden @ W^T at the target, logits never materialised).
+ *   h     bf16 [T,H]    hidden states
+ *   W     bf16 [V,H]    LM-head weight, one row per vocabulary entry
+ *   y     int32 [T]     target ids; rows equal to ignore_index are inactive
+ *   logp  fp32 [T] out  selected log-probability (0 for inactive rows)
+ *   lse   fp32 [T] out  log-sum-exp of the row's logits, the state the
+ *                       backward needs (0 for inactive rows); may be NULL
+ * Requires H % 64 == 0. */
+rlk_status rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* y,
+                               int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                               float* logp, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of L = sum_t g[t] * logp[t] ("Announcing RL-Kernel for vime",
+ * "Key Capabilities": the full-gradient path, gradients reach both the
+ * hidden states and the weight).  Recomputes the logits chunk by chunk; no
+ * atomics, so results are bit-identical across runs.
+ *   lse     fp32 [T]       the forward's lse output (must come from the forward)
+ *   g       fp32 [T]       upstream gradient dL/dlogp
+ *   grad_h  bf16 [T,H] out fp32-accumulated over the whole vocabulary and
+ *                          rounded to bf16 once; zero rows for inactive rows;
+ *                          may be NULL (not computed)
+ *   grad_W  fp32 [V,H] out written once per element; may be NULL
+ * Row ordering: grad_W sums rows in ascending row order. */
+rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y,
+                               const float* lse, const float* g,
+                               int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                               void* grad_h, float* grad_W,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Statistics of one vocabulary range [vocab_start, vocab_start + vocab_len)
+ * of a vocabulary of V_global rows, as one tensor-parallel rank would hold it
+ * ("Why the Fused Path Wins", third reason; "vLLM RL-Kernel v0.1.0 ...",
+ * "Boundary Fixes in the RL-Kernel Strict Path": true vocabulary range,
+ * target ownership, local reduction).
+ *   W_shard  bf16 [vocab_len, H]  rows vocab_start .. vocab_start+vocab_len-1
+ *   y        int32 [T]            GLOBAL target ids
+ *   out      [T]                  per-row statistics (rlk_lse_partial_t)
+ * The range must be an aligned block of splits: with S = ceil(V_global/32)
+ * and n the smallest power of two with n*S >= vocab_len, vocab_start must be
+ * a multiple of n*S and vocab_len == min(vocab_start + n*S, V_global) -
+ * vocab_start; otherwise RLK_ERR_UNALIGNED_VOCAB_RANGE. */
+rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y,
+                           int64_t T, int64_t H,
+                           int64_t vocab_start, int64_t vocab_len, int64_t V_global,
+                           int32_t ignore_index, rlk_lse_partial_t* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Merge of per-range statistics into the selected log-probability ("Why the
+ * Fused Path Wins", third reason: cross-rank log-sum-exp merge).
+ *   parts  [n_parts][T] range statistics in ascending vocabulary order
+ *   logp   fp32 [T] out; lse fp32 [T] out (may be NULL)
+ * Parts are merged with the balanced binary tree (left subtree = the largest
+ * power of two smaller than the count).  When the parts are the n_parts
+ * equal aligned blocks of a power-of-two n_parts <= 32, the result equals
+ * rlk_linear_logp_fwd bit for bit.  1 <= n_parts <= 32. */
+rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts,
+                         const int32_t* y, int64_t T, int32_t ignore_index,
+                         float* logp, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H_ */

@@ -1,0 +1,222 @@
+"""Python binding of librlk.so, the fused deterministic selected-token
+log-probability operator ("linear_logp") for MI355X / gfx950.
+
+Only argument marshalling lives here: every step of the computation runs in
+the HIP kernels behind the C ABI of ``include/rlk.h``.  PyTorch supplies
+device memory, streams and autograd plumbing.  There is no fallback: if the
+library is missing or the device is not gfx950, calls raise.
+
+    logp = linear_logp(h, W, y)            # autograd-aware
+    logp, lse = linear_logp_fwd(h, W, y)
+    grad_h, grad_W = linear_logp_bwd(h, W, y, lse, g)
+    part = lse_partial(h, W_shard, y, vocab_start, V_global)   # [T, 4] records
+    logp, lse = lse_merge(torch.stack(parts), y)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "IGNORE_INDEX", "RlkError", "lib", "library_path", "contract_version",
+    "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
+    "lse_merge", "linear_logp",
+]
+
+IGNORE_INDEX = -100
+OP_FWD, OP_BWD, OP_PARTIAL = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "librlk.so")
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "rlk_contract_version": (_i32, []),
+    "rlk_status_string": (ctypes.c_char_p, [_i32]),
+    "rlk_last_error_message": (ctypes.c_char_p, []),
+    "rlk_workspace_bytes": (_size, [_i32, _i64, _i64, _i64]),
+    "rlk_linear_logp_fwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                                   _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "rlk_linear_logp_bwd": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _i64, _i64, _i64, _i32, _c_void_p, _c_void_p,
+                                   _c_void_p, _size, _c_void_p]),
+    "rlk_lse_partial": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _i64,
+                               _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "rlk_lse_merge": (_i32, [_c_void_p, _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p,
+                             _c_void_p]),
+}
+
+_LIB = None
+
+
+class RlkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        L = lib()
+        msg = L.rlk_status_string(status).decode()
+        detail = L.rlk_last_error_message().decode()
+        super().__init__(f"{where}: status {status} ({msg}){': ' + detail if detail else ''}")
+        self.status = status
+
+
+def lib():
+    """The loaded librlk.so (ctypes), with argument types declared."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run `python -m selected_token_lm_amd.build`")
+        L = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def contract_version() -> int:
+    return int(lib().rlk_contract_version())
+
+
+def workspace_bytes(op: int, T: int, H: int, V: int) -> int:
+    return int(lib().rlk_workspace_bytes(op, T, H, V))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RlkError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _prep(h, W, y):
+    if not (h.is_cuda and W.is_cuda and y.is_cuda):
+        raise ValueError("h, W and y must be device tensors")
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("h and W must be bfloat16")
+    if h.dim() != 2 or W.dim() != 2 or h.shape[1] != W.shape[1]:
+        raise ValueError("h must be [T, H] and W [V, H]")
+    y = y.to(torch.int32) if y.dtype != torch.int32 else y
+    if y.dim() != 1 or y.shape[0] != h.shape[0]:
+        raise ValueError("y must be [T]")
+    return h.contiguous(), W.contiguous(), y.contiguous()
+
+
+def _workspace(op, T, H, V, device):
+    n = workspace_bytes(op, T, H, V)
+    if n == 0:
+        raise ValueError(f"invalid shape T={T} H={H} V={V}")
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def linear_logp_fwd(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None):
+    """Selected-token log-probabilities and log-sum-exp, fp32 [T] each."""
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    logp = torch.empty(T, dtype=torch.float32, device=h.device)
+    lse = torch.empty(T, dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws, n = _workspace(OP_FWD, T, H, V, h.device)
+    else:
+        n = ws.numel()
+    _check(lib().rlk_linear_logp_fwd(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
+                                     _ptr(logp), _ptr(lse), _ptr(ws), n, _stream()),
+           "rlk_linear_logp_fwd")
+    return logp, lse
+
+
+def linear_logp_bwd(h, W, y, lse, g, ignore_index: int = IGNORE_INDEX,
+                    need_grad_h: bool = True, need_grad_W: bool = True, ws=None):
+    """(grad_h bf16 [T,H] or None, grad_W fp32 [V,H] or None) of sum_t g_t logp_t."""
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    lse = lse.to(torch.float32).contiguous()
+    g = g.to(torch.float32).contiguous()
+    grad_h = torch.empty((T, H), dtype=torch.bfloat16, device=h.device) if need_grad_h else None
+    grad_W = torch.empty((V, H), dtype=torch.float32, device=h.device) if need_grad_W else None
+    if ws is None:
+        ws, n = _workspace(OP_BWD, T, H, V, h.device)
+    else:
+        n = ws.numel()
+    _check(lib().rlk_linear_logp_bwd(_ptr(h), _ptr(W), _ptr(y), _ptr(lse), _ptr(g), T, H, V,
+                                     ignore_index, _ptr(grad_h), _ptr(grad_W), _ptr(ws), n,
+                                     _stream()),
+           "rlk_linear_logp_bwd")
+    return grad_h, grad_W
+
+
+def lse_partial(h, W_shard, y, vocab_start: int, V_global: int,
+                ignore_index: int = IGNORE_INDEX, ws=None):
+    """Per-row statistics of the range [vocab_start, vocab_start + len(W_shard)).
+
+    Returns a float32 tensor [T, 4] holding (m, s, z_target, owned) per row;
+    the last column holds uint32 bits (view it with ``.view(torch.int32)``).
+    """
+    h, W_shard, y = _prep(h, W_shard, y)
+    T, H = h.shape
+    n_rows = W_shard.shape[0]
+    out = torch.empty((T, 4), dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws, n = _workspace(OP_PARTIAL, T, H, V_global, h.device)
+    else:
+        n = ws.numel()
+    _check(lib().rlk_lse_partial(_ptr(h), _ptr(W_shard), _ptr(y), T, H, vocab_start, n_rows,
+                                 V_global, ignore_index, _ptr(out), _ptr(ws), n, _stream()),
+           "rlk_lse_partial")
+    return out
+
+
+def lse_merge(parts, y, ignore_index: int = IGNORE_INDEX):
+    """Merge [P, T, 4] range statistics (ascending vocabulary order) into (logp, lse)."""
+    if parts.dim() != 3 or parts.shape[2] != 4 or parts.dtype != torch.float32:
+        raise ValueError("parts must be float32 [P, T, 4]")
+    y = (y.to(torch.int32) if y.dtype != torch.int32 else y).contiguous()
+    parts = parts.contiguous()
+    P, T = parts.shape[0], parts.shape[1]
+    logp = torch.empty(T, dtype=torch.float32, device=parts.device)
+    lse = torch.empty(T, dtype=torch.float32, device=parts.device)
+    _check(lib().rlk_lse_merge(_ptr(parts), P, _ptr(y), T, ignore_index, _ptr(logp), _ptr(lse),
+                               _stream()),
+           "rlk_lse_merge")
+    return logp, lse
+
+
+class _LinearLogp(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, h, W, y, ignore_index):
+        logp, lse = linear_logp_fwd(h, W, y, ignore_index)
+        ctx.save_for_backward(h, W, y, lse)
+        ctx.ignore_index = ignore_index
+        return logp
+
+    @staticmethod
+    def backward(ctx, g):
+        h, W, y, lse = ctx.saved_tensors
+        gh, gW = linear_logp_bwd(h, W, y, lse, g, ctx.ignore_index,
+                                 need_grad_h=ctx.needs_input_grad[0],
+                                 need_grad_W=ctx.needs_input_grad[1])
+        if gW is not None:
+            gW = gW.to(W.dtype)
+        return gh, gW, None, None
+
+
+def linear_logp(h, W, y, ignore_index: int = IGNORE_INDEX):
+    """log_softmax(h @ W^T)[t, y_t] per row (0 where y_t == ignore_index), autograd-aware.
+
+    The weight gradient is computed in fp32 and cast to W's dtype for
+    autograd; call ``linear_logp_bwd`` directly to keep it in fp32.
+    """
+    return _LinearLogp.apply(h, W, y, ignore_index)

@@ -1,0 +1,359 @@
+// Host side of the C ABI declared in include/rlk.h: argument validation,
+// workspace layout and kernel launches.  Everything is enqueued on the
+// caller's stream; nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/rlk.h"
+#include "rlk_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rlk_status fail(rlk_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rlk_status fail(rlk_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+rlk_status ok() {
+  g_last_error.clear();
+  return RLK_OK;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Limits that keep every 32-bit index inside the kernels in range.
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int64_t kMaxH = 1 << 16;
+constexpr int64_t kMaxV = 8000000;  // 32 splits x chunks stay within one grid dimension
+
+struct Geom {
+  int64_t V, S, cps, S_pad;
+};
+
+Geom geom_of(int64_t V_global) {
+  Geom g;
+  g.V = V_global;
+  g.S = ceil_div(V_global, rlk::kNSplit);
+  g.cps = ceil_div(g.S, rlk::kChunk);
+  g.S_pad = g.cps * rlk::kChunk;
+  return g;
+}
+
+// --- workspace layouts -------------------------------------------------------
+struct FwdWs {
+  size_t idx, n_act, zt, rec, total;
+  int64_t rec_chunks;
+};
+
+// Record slots: one per (chunk of the full vocabulary of V rows, row).
+FwdWs fwd_layout(int64_t T, int64_t V) {
+  FwdWs w;
+  size_t off = 0;
+  w.idx = off;
+  off = align256(off + sizeof(int32_t) * T);
+  w.n_act = off;
+  off = align256(off + sizeof(int32_t));
+  w.zt = off;
+  off = align256(off + sizeof(float) * T);
+  w.rec_chunks = rlk::kNSplit * geom_of(V).cps;
+  w.rec = off;
+  off = align256(off + sizeof(float2) * (size_t)w.rec_chunks * (size_t)T);
+  w.total = off;
+  return w;
+}
+
+struct BwdWs {
+  size_t idx, n_act, hT, WT, dZ, dZT, ghacc, total;
+  int64_t T_pad;
+};
+
+BwdWs bwd_layout(int64_t T, int64_t H, int64_t V) {
+  const Geom g = geom_of(V);
+  BwdWs w;
+  w.T_pad = ceil_div(T, rlk::kBM) * rlk::kBM;
+  size_t off = 0;
+  w.idx = off;
+  off = align256(off + sizeof(int32_t) * T);
+  w.n_act = off;
+  off = align256(off + sizeof(int32_t));
+  w.hT = off;
+  off = align256(off + 2 * (size_t)H * w.T_pad);
+  w.WT = off;
+  off = align256(off + 2 * (size_t)rlk::kNSplit * H * g.S_pad);
+  w.dZ = off;
+  off = align256(off + 2 * (size_t)w.T_pad * g.S_pad);
+  w.dZT = off;
+  off = align256(off + 2 * (size_t)g.S_pad * w.T_pad);
+  w.ghacc = off;
+  off = align256(off + 4 * (size_t)T * H);
+  w.total = off;
+  return w;
+}
+
+// --- device check ----------------------------------------------------------------
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+rlk_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RLK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(RLK_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (g_dev_ok[dev] < 0) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (g_dev_ok[dev] < 0) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  return RLK_OK;
+}
+
+rlk_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return RLK_OK;
+}
+
+#define RLK_TRY(x)                  \
+  do {                              \
+    rlk_status _s = (x);            \
+    if (_s != RLK_OK) return _s;    \
+  } while (0)
+
+rlk_status check_common(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V) {
+  if (!h || !W || !y) return fail(RLK_ERR_NULL_ARG, "h, W and y are required");
+  if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
+  if (H <= 0 || H > kMaxH || H % 64 != 0)
+    return fail(RLK_ERR_BAD_SHAPE, "H=%lld must be a positive multiple of 64 up to 65536", (long long)H);
+  if (V <= 0 || V > kMaxV) return fail(RLK_ERR_BAD_SHAPE, "V=%lld out of [1, 8000000]", (long long)V);
+  if (!aligned16(h) || !aligned16(W) || !aligned16(y)) return fail(RLK_ERR_BAD_ALIGNMENT, "h, W, y must be 16-byte aligned");
+  return RLK_OK;
+}
+
+// Split range [s0, s0 + n) of an aligned vocabulary block, or an error.
+rlk_status split_range(int64_t vocab_start, int64_t vocab_len, int64_t V_global, int* s0, int* n) {
+  const Geom g = geom_of(V_global);
+  if (vocab_start < 0 || vocab_len <= 0 || vocab_start + vocab_len > V_global)
+    return fail(RLK_ERR_UNALIGNED_VOCAB_RANGE, "range [%lld, +%lld) not inside [0, %lld)", (long long)vocab_start,
+                (long long)vocab_len, (long long)V_global);
+  int64_t nn = 1;
+  while (nn * g.S < vocab_len) nn <<= 1;
+  if (nn > rlk::kNSplit || vocab_start % (nn * g.S) != 0 ||
+      vocab_len != std::min(vocab_start + nn * g.S, V_global) - vocab_start)
+    return fail(RLK_ERR_UNALIGNED_VOCAB_RANGE,
+                "range [%lld, +%lld) is not an aligned block of splits (split width %lld)", (long long)vocab_start,
+                (long long)vocab_len, (long long)g.S);
+  *s0 = (int)(vocab_start / g.S);
+  *n = (int)nn;
+  return RLK_OK;
+}
+
+// Shared forward body: statistics of splits [s0, s0+n) then the epilogue.
+rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V_global,
+                       int32_t ignore_index, int s0, int nsplit, int64_t vocab_start, int64_t vocab_len, int mode,
+                       float* logp, float* lse, rlk_lse_partial_t* pout, void* ws, hipStream_t st) {
+  const Geom g = geom_of(V_global);
+  const FwdWs L = fwd_layout(T, V_global);
+  char* base = static_cast<char*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+  int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
+  float* zt = reinterpret_cast<float*>(base + L.zt);
+  float2* rec = reinterpret_cast<float2*>(base + L.rec);
+  rlk::PartialRec* pr = reinterpret_cast<rlk::PartialRec*>(pout);
+
+  hipLaunchKernelGGL(rlk::compact_rows, dim3(1), dim3(1024), 0, st, y, (int)T, ignore_index, idx, n_act,
+                     mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
+  RLK_TRY(launched("compact_rows"));
+
+  rlk::SplitGeom gm;
+  gm.V = (int)g.V;
+  gm.S = (int)g.S;
+  gm.cps = (int)g.cps;
+  gm.s0 = s0;
+  gm.vocab_start = (int)vocab_start;
+  const int64_t nchunks = (int64_t)nsplit * g.cps;
+  dim3 grid((unsigned)ceil_div(T, rlk::kBM), (unsigned)nchunks);
+  hipLaunchKernelGGL(rlk::fwd_chunks, grid, dim3(rlk::kThreads), 0, st, static_cast<const uint16_t*>(h),
+                     static_cast<const uint16_t*>(W), y, idx, n_act, (int)H, gm, (size_t)T, rec, zt);
+  RLK_TRY(launched("fwd_chunks"));
+
+  hipLaunchKernelGGL(rlk::merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), 0, st, rec, (size_t)T, zt, idx,
+                     n_act, y, gm, nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
+  return launched("merge_splits");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rlk_contract_version(void) { return RLK_CONTRACT_VERSION; }
+
+const char* rlk_status_string(rlk_status s) {
+  switch (s) {
+    case RLK_OK: return "ok";
+    case RLK_ERR_NULL_ARG: return "a required pointer is NULL";
+    case RLK_ERR_BAD_SHAPE: return "invalid shape";
+    case RLK_ERR_BAD_ALIGNMENT: return "pointer not 16-byte aligned";
+    case RLK_ERR_UNALIGNED_VOCAB_RANGE: return "vocabulary range is not an aligned block of splits";
+    case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RLK_ERR_HIP: return "HIP runtime error";
+    case RLK_ERR_UNSUPPORTED_DEVICE: return "device is not gfx950";
+    case RLK_ERR_BAD_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* rlk_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t rlk_workspace_bytes(int32_t op, int64_t T, int64_t H, int64_t V) {
+  if (T < 0 || T > kMaxT || H <= 0 || H > kMaxH || H % 64 != 0 || V <= 0 || V > kMaxV) return 0;
+  switch (op) {
+    case RLK_OP_FWD:
+    case RLK_OP_PARTIAL: return fwd_layout(T, V).total;
+    case RLK_OP_BWD: return bwd_layout(T, H, V).total;
+    default: return 0;
+  }
+}
+
+rlk_status rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V,
+                               int32_t ignore_index, float* logp, float* lse, void* ws, size_t ws_bytes,
+                               void* stream) {
+  RLK_TRY(check_common(h, W, y, T, H, V));
+  if (!logp || !ws) return fail(RLK_ERR_NULL_ARG, "logp and ws are required");
+  if (!aligned16(logp) || (lse && !aligned16(lse)) || !aligned16(ws))
+    return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse, ws must be 16-byte aligned");
+  if (ws_bytes < fwd_layout(T, V).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V).total, ws_bytes);
+  if (T == 0) return ok();
+  RLK_TRY(check_device());
+  RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
+                      static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y, int64_t T, int64_t H,
+                           int64_t vocab_start, int64_t vocab_len, int64_t V_global, int32_t ignore_index,
+                           rlk_lse_partial_t* out, void* ws, size_t ws_bytes, void* stream) {
+  RLK_TRY(check_common(h, W_shard, y, T, H, V_global));
+  if (!out || !ws) return fail(RLK_ERR_NULL_ARG, "out and ws are required");
+  if (!aligned16(out) || !aligned16(ws)) return fail(RLK_ERR_BAD_ALIGNMENT, "out, ws must be 16-byte aligned");
+  int s0 = 0, n = 0;
+  RLK_TRY(split_range(vocab_start, vocab_len, V_global, &s0, &n));
+  if (ws_bytes < fwd_layout(T, V_global).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V_global).total, ws_bytes);
+  if (T == 0) return ok();
+  RLK_TRY(check_device());
+  RLK_TRY(run_forward(h, W_shard, y, T, H, V_global, ignore_index, s0, n, vocab_start, vocab_len, 1, nullptr, nullptr,
+                      out, ws, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts, const int32_t* y, int64_t T,
+                         int32_t ignore_index, float* logp, float* lse, void* stream) {
+  if (!parts || !y || !logp) return fail(RLK_ERR_NULL_ARG, "parts, y and logp are required");
+  if (n_parts < 1 || n_parts > rlk::kNSplit) return fail(RLK_ERR_BAD_ARG, "n_parts=%d out of [1, 32]", n_parts);
+  if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
+  if (!aligned16(parts) || !aligned16(y) || !aligned16(logp) || (lse && !aligned16(lse)))
+    return fail(RLK_ERR_BAD_ALIGNMENT, "parts, y, logp, lse must be 16-byte aligned");
+  if (T == 0) return ok();
+  RLK_TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(rlk::merge_parts, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st,
+                     reinterpret_cast<const rlk::PartialRec*>(parts), n_parts, (int)T, y, ignore_index, logp, lse);
+  RLK_TRY(launched("merge_parts"));
+  return ok();
+}
+
+rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, const float* lse, const float* g,
+                               int64_t T, int64_t H, int64_t V, int32_t ignore_index, void* grad_h, float* grad_W,
+                               void* ws, size_t ws_bytes, void* stream) {
+  RLK_TRY(check_common(h, W, y, T, H, V));
+  if (!lse || !g || !ws) return fail(RLK_ERR_NULL_ARG, "lse, g and ws are required");
+  if (!aligned16(lse) || !aligned16(g) || !aligned16(ws) || (grad_h && !aligned16(grad_h)) ||
+      (grad_W && !aligned16(grad_W)))
+    return fail(RLK_ERR_BAD_ALIGNMENT, "lse, g, ws, grad_h, grad_W must be 16-byte aligned");
+  const BwdWs L = bwd_layout(T, H, V);
+  if (ws_bytes < L.total) return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", L.total, ws_bytes);
+  if (T == 0) return ok();
+  if (!grad_h && !grad_W) return ok();
+  RLK_TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Geom gg = geom_of(V);
+  char* base = static_cast<char*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+  int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.hT);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(base + L.WT);
+  uint16_t* dZ = reinterpret_cast<uint16_t*>(base + L.dZ);
+  uint16_t* dZT = reinterpret_cast<uint16_t*>(base + L.dZT);
+  float* ghacc = reinterpret_cast<float*>(base + L.ghacc);
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  const uint16_t* Wb = static_cast<const uint16_t*>(W);
+
+  hipLaunchKernelGGL(rlk::compact_rows, dim3(1), dim3(1024), 0, st, y, (int)T, ignore_index, idx, n_act, nullptr,
+                     nullptr, nullptr);
+  RLK_TRY(launched("compact_rows"));
+  if (grad_W) {
+    hipLaunchKernelGGL(rlk::transpose_h, dim3((unsigned)(L.T_pad / 64), (unsigned)(H / 64)), dim3(256), 0, st, hb, idx,
+                       n_act, (int)H, (int)L.T_pad, hT);
+    RLK_TRY(launched("transpose_h"));
+  }
+  if (grad_h) {
+    hipLaunchKernelGGL(rlk::transpose_w, dim3((unsigned)(gg.S_pad / 64), (unsigned)(H / 64), rlk::kNSplit), dim3(256),
+                       0, st, Wb, (int)V, (int)H, (int)gg.S, (int)gg.S_pad, WT);
+    RLK_TRY(launched("transpose_w"));
+    hipLaunchKernelGGL(rlk::zero_rows, dim3((unsigned)T), dim3(256), 0, st, y, ignore_index, (int)H,
+                       static_cast<uint16_t*>(grad_h));
+    RLK_TRY(launched("zero_rows"));
+  }
+  rlk::SplitGeom gm;
+  gm.V = (int)gg.V;
+  gm.S = (int)gg.S;
+  gm.cps = (int)gg.cps;
+  gm.s0 = 0;
+  gm.vocab_start = 0;
+  int last_split = 0;
+  for (int c = 0; c < rlk::kNSplit; ++c)
+    if ((int64_t)c * gg.S < V) last_split = c;
+  const unsigned row_tiles = (unsigned)ceil_div(T, rlk::kBM);
+  const unsigned h_tiles = (unsigned)ceil_div(H, rlk::kBN);
+  for (int c = 0; c <= last_split; ++c) {
+    const int valid = (int)std::min<int64_t>(gg.S, V - (int64_t)c * gg.S);
+    hipLaunchKernelGGL(rlk::dz_tile, dim3(row_tiles, (unsigned)gg.cps), dim3(rlk::kThreads), 0, st, hb, Wb, y, idx,
+                       n_act, lse, g, (int)H, gm, c, (int)L.T_pad, (int)gg.S_pad, dZ, dZT);
+    RLK_TRY(launched("dz_tile"));
+    if (grad_W) {
+      hipLaunchKernelGGL(rlk::grad_w_tile, dim3((unsigned)gg.cps, h_tiles), dim3(rlk::kThreads), 0, st, dZT, hT,
+                         n_act, (int)H, (int)L.T_pad, valid, (size_t)c * gg.S, grad_W);
+      RLK_TRY(launched("grad_w_tile"));
+    }
+    if (grad_h) {
+      hipLaunchKernelGGL(rlk::grad_h_tile, dim3(row_tiles, h_tiles), dim3(rlk::kThreads), 0, st, dZ,
+                         WT + (size_t)c * H * gg.S_pad, idx, n_act, (int)H, (int)gg.S_pad, c == 0 ? 1 : 0,
+                         c == last_split ? 1 : 0, ghacc, static_cast<uint16_t*>(grad_h));
+      RLK_TRY(launched("grad_h_tile"));
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and host-side validation rejects bad arguments before touching the device.
+
+Fake pointers below are never dereferenced: each call is built so that a
+host check fails (or T == 0) before any HIP call or kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selected_token_lm_amd as rlk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlk.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_ALIGN, UNALIGNED_RANGE, WS_SMALL, HIP, DEVICE, BAD_ARG = range(9)
+
+FAKE = 0x100000      # 16-byte aligned, never dereferenced
+MISALIGNED = 0x100008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlk_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(rlk.library_path)
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(rlk._SIGNATURES)
+
+
+def test_contract_version_and_status_strings():
+    L = rlk.lib()
+    assert L.rlk_contract_version() == 1
+    for s in range(9):
+        assert len(L.rlk_status_string(s)) > 0
+    assert L.rlk_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    W = rlk.workspace_bytes
+    assert W(0, 4096, 4096, 151936) >= 32 * 38 * 4096 * 8
+    assert W(2, 4096, 4096, 151936) == W(0, 4096, 4096, 151936)
+    bwd = W(1, 4096, 4096, 151936)
+    # transposed weight copy (32 splits x H x padded split) dominates
+    assert bwd >= 2 * 32 * 4096 * 4864
+    assert W(0, 0, 64, 10) > 0
+    for bad in [(0, -1, 64, 10), (0, 4, 63, 10), (0, 4, 0, 10), (0, 4, 64, 0), (7, 4, 64, 10),
+                (0, 4, 64, 8_000_001)]:
+        assert W(*bad) == 0, bad
+
+
+def fwd(h=FAKE, W=FAKE, y=FAKE, T=64, H=256, V=4096, logp=FAKE, lse=FAKE, ws=FAKE, nbytes=1 << 40):
+    return rlk.lib().rlk_linear_logp_fwd(h, W, y, T, H, V, -100, logp, lse, ws, nbytes, None)
+
+
+def test_fwd_validation():
+    assert fwd(h=None) == NULL_ARG
+    assert fwd(W=None) == NULL_ARG
+    assert fwd(y=None) == NULL_ARG
+    assert fwd(logp=None) == NULL_ARG
+    assert fwd(ws=None) == NULL_ARG
+    assert fwd(T=-1) == BAD_SHAPE
+    assert fwd(H=0) == BAD_SHAPE
+    assert fwd(H=96) == BAD_SHAPE
+    assert fwd(V=0) == BAD_SHAPE
+    assert fwd(V=9_000_000) == BAD_SHAPE
+    assert fwd(h=MISALIGNED) == BAD_ALIGN
+    assert fwd(lse=MISALIGNED) == BAD_ALIGN
+    assert fwd(nbytes=100) == WS_SMALL
+    assert b"need" in rlk.lib().rlk_last_error_message()
+    # T == 0: nothing to do, nothing launched
+    assert fwd(T=0, nbytes=rlk.workspace_bytes(0, 0, 256, 4096)) == OK
+    assert rlk.lib().rlk_last_error_message() == b""
+
+
+def bwd(h=FAKE, W=FAKE, y=FAKE, lse=FAKE, g=FAKE, T=64, H=256, V=4096, gh=FAKE, gW=FAKE, ws=FAKE,
+        nbytes=1 << 40):
+    return rlk.lib().rlk_linear_logp_bwd(h, W, y, lse, g, T, H, V, -100, gh, gW, ws, nbytes, None)
+
+
+def test_bwd_validation():
+    assert bwd(lse=None) == NULL_ARG
+    assert bwd(g=None) == NULL_ARG
+    assert bwd(ws=None) == NULL_ARG
+    assert bwd(H=100) == BAD_SHAPE
+    assert bwd(gW=MISALIGNED) == BAD_ALIGN
+    assert bwd(nbytes=1 << 20) == WS_SMALL
+    assert bwd(T=0, nbytes=rlk.workspace_bytes(1, 0, 256, 4096)) == OK
+
+
+def partial(start, length, Vg=151936, T=16, H=64, out=FAKE, nbytes=1 << 40):
+    return rlk.lib().rlk_lse_partial(FAKE, FAKE, FAKE, T, H, start, length, Vg, -100, out, FAKE,
+                                     nbytes, None)
+
+
+def test_partial_range_alignment():
+    # S = ceil(151936 / 32) = 4748; aligned power-of-two blocks of splits are accepted
+    # (checked with T == 0 so nothing is launched)
+    for start, length in [(0, 151936), (0, 75968), (75968, 75968), (4748 * 3, 4748),
+                          (4748 * 8, 4748 * 8), (4748 * 30, 4748 * 2)]:
+        assert partial(start, length, T=0) == OK, (start, length)
+    for start, length in [(1, 4748), (0, 4747), (4748, 2 * 4748), (0, 3 * 4748), (75968, 75967),
+                          (-4748, 4748), (0, 0), (151936 - 4748, 2 * 4748)]:
+        assert partial(start, length) == UNALIGNED_RANGE, (start, length)
+    # a vocabulary that is not a multiple of 32: the last block is short
+    Vg = 151937  # S = 4749
+    assert partial(75984, 151937 - 75984, Vg=Vg, T=0) == OK
+    assert partial(75984, 75984, Vg=Vg) == UNALIGNED_RANGE
+    assert partial(0, 75968, out=None) == NULL_ARG
+    assert partial(0, 75968, nbytes=16) == WS_SMALL
+
+
+def test_merge_validation():
+    L = rlk.lib()
+    assert L.rlk_lse_merge(None, 2, FAKE, 8, -100, FAKE, FAKE, None) == NULL_ARG
+    assert L.rlk_lse_merge(FAKE, 0, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ARG
+    assert L.rlk_lse_merge(FAKE, 33, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ARG
+    assert L.rlk_lse_merge(FAKE, 2, FAKE, -1, -100, FAKE, FAKE, None) == BAD_SHAPE
+    assert L.rlk_lse_merge(MISALIGNED, 2, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ALIGN
+    assert L.rlk_lse_merge(FAKE, 2, FAKE, 0, -100, FAKE, FAKE, None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    h = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rlk.linear_logp_fwd(h, h, torch.zeros(4, dtype=torch.int32))
