@@ -46,7 +46,8 @@
  *   - host-detectable errors return a status and enqueue nothing; data errors
  *     the host cannot see (a target outside [0,V) that is not ignore_index,
  *     or no part owning an active target) give NaN in that row's logp;
- *   - T == 0 returns RLK_OK without launching anything.
+ *   - T == 0 returns RLK_OK without launching anything (after the shape
+ *     checks); row-indexed pointers may then be NULL.
  */
 #ifndef RLK_H_
 #define RLK_H_
@@ -166,6 +167,22 @@ rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y,
 rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts,
                          const int32_t* y, int64_t T, int32_t ignore_index,
                          float* logp, float* lse, void* stream);
+
+/* Per-kernel timing for benchmarks; computes nothing.  After
+ * rlk_profile_begin(), every kernel the library launches (on any stream) is
+ * bracketed by two HIP events recorded on that stream.  rlk_profile_end()
+ * waits for those events, turns timing off and writes up to max_entries
+ * per-kernel totals to `out` (launch count and summed event time in ms);
+ * *n_entries receives the number of distinct kernels seen.  Not meant to be
+ * used from several threads at once. */
+typedef struct {
+  char name[40];
+  int64_t launches;
+  double total_ms;
+} rlk_kernel_time_t;
+
+rlk_status rlk_profile_begin(void);
+rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t* n_entries);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "IGNORE_INDEX", "RlkError", "lib", "library_path", "contract_version",
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
-    "lse_merge", "linear_logp",
+    "lse_merge", "linear_logp", "profile_begin", "profile_end",
 ]
 
 IGNORE_INDEX = -100
@@ -50,7 +50,13 @@ _SIGNATURES = {
                                _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
     "rlk_lse_merge": (_i32, [_c_void_p, _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p,
                              _c_void_p]),
+    "rlk_profile_begin": (_i32, []),
+    "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
 }
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 _LIB = None
 
@@ -192,6 +198,20 @@ def lse_merge(parts, y, ignore_index: int = IGNORE_INDEX):
                                _stream()),
            "rlk_lse_merge")
     return logp, lse
+
+
+def profile_begin():
+    """Start timing every kernel the library launches (HIP events on its stream)."""
+    _check(lib().rlk_profile_begin(), "rlk_profile_begin")
+
+
+def profile_end():
+    """Stop timing; {kernel name: (launches, total ms)} since profile_begin()."""
+    buf = (KernelTime * 64)()
+    n = _i32(0)
+    _check(lib().rlk_profile_end(buf, 64, ctypes.byref(n)), "rlk_profile_end")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n.value, 64))}
 
 
 class _LinearLogp(torch.autograd.Function):

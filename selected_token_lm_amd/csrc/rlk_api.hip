@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/rlk.h"
 #include "rlk_kernels.h"
@@ -133,18 +134,72 @@ rlk_status launched(const char* what) {
   return RLK_OK;
 }
 
+// --- optional per-kernel timing (rlk_profile_begin / rlk_profile_end) ---------
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events on its stream when timing is enabled.
+struct ProfScope {
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(const char* n, hipStream_t s) : name(n), st(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    a = prof_event();
+    b = prof_event();
+    if (a && b) (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a || !b) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    (void)hipEventRecord(b, st);
+    g_prof_recs.push_back(ProfRec{name, a, b});
+  }
+};
+
 #define RLK_TRY(x)                  \
   do {                              \
     rlk_status _s = (x);            \
     if (_s != RLK_OK) return _s;    \
   } while (0)
 
+// Launch a kernel on stream `st`, timed when profiling is on; return on error.
+#define RLK_LAUNCH(kern, grid, block, st, ...)                        \
+  do {                                                                \
+    {                                                                 \
+      ProfScope _ps(#kern, st);                                       \
+      hipLaunchKernelGGL(rlk::kern, grid, block, 0, st, __VA_ARGS__); \
+    }                                                                 \
+    RLK_TRY(launched(#kern));                                         \
+  } while (0)
+
+// Shapes first; with T == 0 there is nothing to read or write, so the
+// pointers are not checked (empty tensors may carry NULL).
 rlk_status check_common(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V) {
-  if (!h || !W || !y) return fail(RLK_ERR_NULL_ARG, "h, W and y are required");
   if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
   if (H <= 0 || H > kMaxH || H % 64 != 0)
     return fail(RLK_ERR_BAD_SHAPE, "H=%lld must be a positive multiple of 64 up to 65536", (long long)H);
   if (V <= 0 || V > kMaxV) return fail(RLK_ERR_BAD_SHAPE, "V=%lld out of [1, 8000000]", (long long)V);
+  if (T == 0) return RLK_OK;
+  if (!h || !W || !y) return fail(RLK_ERR_NULL_ARG, "h, W and y are required");
   if (!aligned16(h) || !aligned16(W) || !aligned16(y)) return fail(RLK_ERR_BAD_ALIGNMENT, "h, W, y must be 16-byte aligned");
   return RLK_OK;
 }
@@ -180,9 +235,8 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   float2* rec = reinterpret_cast<float2*>(base + L.rec);
   rlk::PartialRec* pr = reinterpret_cast<rlk::PartialRec*>(pout);
 
-  hipLaunchKernelGGL(rlk::compact_rows, dim3(1), dim3(1024), 0, st, y, (int)T, ignore_index, idx, n_act,
-                     mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
-  RLK_TRY(launched("compact_rows"));
+  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, n_act,
+             mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
 
   rlk::SplitGeom gm;
   gm.V = (int)g.V;
@@ -192,13 +246,12 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   gm.vocab_start = (int)vocab_start;
   const int64_t nchunks = (int64_t)nsplit * g.cps;
   dim3 grid((unsigned)ceil_div(T, rlk::kBM), (unsigned)nchunks);
-  hipLaunchKernelGGL(rlk::fwd_chunks, grid, dim3(rlk::kThreads), 0, st, static_cast<const uint16_t*>(h),
-                     static_cast<const uint16_t*>(W), y, idx, n_act, (int)H, gm, (size_t)T, rec, zt);
-  RLK_TRY(launched("fwd_chunks"));
+  RLK_LAUNCH(fwd_chunks, grid, dim3(rlk::kThreads), st, static_cast<const uint16_t*>(h),
+             static_cast<const uint16_t*>(W), y, idx, n_act, (int)H, gm, (size_t)T, rec, zt);
 
-  hipLaunchKernelGGL(rlk::merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), 0, st, rec, (size_t)T, zt, idx,
-                     n_act, y, gm, nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
-  return launched("merge_splits");
+  RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
+             nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
+  return RLK_OK;
 }
 
 }  // namespace
@@ -238,12 +291,12 @@ rlk_status rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* y, i
                                int32_t ignore_index, float* logp, float* lse, void* ws, size_t ws_bytes,
                                void* stream) {
   RLK_TRY(check_common(h, W, y, T, H, V));
+  if (T == 0) return ok();
   if (!logp || !ws) return fail(RLK_ERR_NULL_ARG, "logp and ws are required");
   if (!aligned16(logp) || (lse && !aligned16(lse)) || !aligned16(ws))
     return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse, ws must be 16-byte aligned");
   if (ws_bytes < fwd_layout(T, V).total)
     return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V).total, ws_bytes);
-  if (T == 0) return ok();
   RLK_TRY(check_device());
   RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
                       static_cast<hipStream_t>(stream)));
@@ -254,13 +307,13 @@ rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y,
                            int64_t vocab_start, int64_t vocab_len, int64_t V_global, int32_t ignore_index,
                            rlk_lse_partial_t* out, void* ws, size_t ws_bytes, void* stream) {
   RLK_TRY(check_common(h, W_shard, y, T, H, V_global));
-  if (!out || !ws) return fail(RLK_ERR_NULL_ARG, "out and ws are required");
-  if (!aligned16(out) || !aligned16(ws)) return fail(RLK_ERR_BAD_ALIGNMENT, "out, ws must be 16-byte aligned");
   int s0 = 0, n = 0;
   RLK_TRY(split_range(vocab_start, vocab_len, V_global, &s0, &n));
+  if (T == 0) return ok();
+  if (!out || !ws) return fail(RLK_ERR_NULL_ARG, "out and ws are required");
+  if (!aligned16(out) || !aligned16(ws)) return fail(RLK_ERR_BAD_ALIGNMENT, "out, ws must be 16-byte aligned");
   if (ws_bytes < fwd_layout(T, V_global).total)
     return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V_global).total, ws_bytes);
-  if (T == 0) return ok();
   RLK_TRY(check_device());
   RLK_TRY(run_forward(h, W_shard, y, T, H, V_global, ignore_index, s0, n, vocab_start, vocab_len, 1, nullptr, nullptr,
                       out, ws, static_cast<hipStream_t>(stream)));
@@ -269,17 +322,16 @@ rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y,
 
 rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts, const int32_t* y, int64_t T,
                          int32_t ignore_index, float* logp, float* lse, void* stream) {
-  if (!parts || !y || !logp) return fail(RLK_ERR_NULL_ARG, "parts, y and logp are required");
   if (n_parts < 1 || n_parts > rlk::kNSplit) return fail(RLK_ERR_BAD_ARG, "n_parts=%d out of [1, 32]", n_parts);
   if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
+  if (T == 0) return ok();
+  if (!parts || !y || !logp) return fail(RLK_ERR_NULL_ARG, "parts, y and logp are required");
   if (!aligned16(parts) || !aligned16(y) || !aligned16(logp) || (lse && !aligned16(lse)))
     return fail(RLK_ERR_BAD_ALIGNMENT, "parts, y, logp, lse must be 16-byte aligned");
-  if (T == 0) return ok();
   RLK_TRY(check_device());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(rlk::merge_parts, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st,
-                     reinterpret_cast<const rlk::PartialRec*>(parts), n_parts, (int)T, y, ignore_index, logp, lse);
-  RLK_TRY(launched("merge_parts"));
+  RLK_LAUNCH(merge_parts, dim3((unsigned)ceil_div(T, 256)), dim3(256), st,
+             reinterpret_cast<const rlk::PartialRec*>(parts), n_parts, (int)T, y, ignore_index, logp, lse);
   return ok();
 }
 
@@ -287,13 +339,13 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
                                int64_t T, int64_t H, int64_t V, int32_t ignore_index, void* grad_h, float* grad_W,
                                void* ws, size_t ws_bytes, void* stream) {
   RLK_TRY(check_common(h, W, y, T, H, V));
+  if (T == 0) return ok();
   if (!lse || !g || !ws) return fail(RLK_ERR_NULL_ARG, "lse, g and ws are required");
   if (!aligned16(lse) || !aligned16(g) || !aligned16(ws) || (grad_h && !aligned16(grad_h)) ||
       (grad_W && !aligned16(grad_W)))
     return fail(RLK_ERR_BAD_ALIGNMENT, "lse, g, ws, grad_h, grad_W must be 16-byte aligned");
   const BwdWs L = bwd_layout(T, H, V);
   if (ws_bytes < L.total) return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", L.total, ws_bytes);
-  if (T == 0) return ok();
   if (!grad_h && !grad_W) return ok();
   RLK_TRY(check_device());
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -309,21 +361,15 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
 
-  hipLaunchKernelGGL(rlk::compact_rows, dim3(1), dim3(1024), 0, st, y, (int)T, ignore_index, idx, n_act, nullptr,
-                     nullptr, nullptr);
-  RLK_TRY(launched("compact_rows"));
+  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, n_act, nullptr, nullptr, nullptr);
   if (grad_W) {
-    hipLaunchKernelGGL(rlk::transpose_h, dim3((unsigned)(L.T_pad / 64), (unsigned)(H / 64)), dim3(256), 0, st, hb, idx,
-                       n_act, (int)H, (int)L.T_pad, hT);
-    RLK_TRY(launched("transpose_h"));
+    RLK_LAUNCH(transpose_h, dim3((unsigned)(L.T_pad / 64), (unsigned)(H / 64)), dim3(256), st, hb, idx, n_act,
+               (int)H, (int)L.T_pad, hT);
   }
   if (grad_h) {
-    hipLaunchKernelGGL(rlk::transpose_w, dim3((unsigned)(gg.S_pad / 64), (unsigned)(H / 64), rlk::kNSplit), dim3(256),
-                       0, st, Wb, (int)V, (int)H, (int)gg.S, (int)gg.S_pad, WT);
-    RLK_TRY(launched("transpose_w"));
-    hipLaunchKernelGGL(rlk::zero_rows, dim3((unsigned)T), dim3(256), 0, st, y, ignore_index, (int)H,
-                       static_cast<uint16_t*>(grad_h));
-    RLK_TRY(launched("zero_rows"));
+    RLK_LAUNCH(transpose_w, dim3((unsigned)(gg.S_pad / 64), (unsigned)(H / 64), rlk::kNSplit), dim3(256), st, Wb,
+               (int)V, (int)H, (int)gg.S, (int)gg.S_pad, WT);
+    RLK_LAUNCH(zero_rows, dim3((unsigned)T), dim3(256), st, y, ignore_index, (int)H, static_cast<uint16_t*>(grad_h));
   }
   rlk::SplitGeom gm;
   gm.V = (int)gg.V;
@@ -338,22 +384,58 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   const unsigned h_tiles = (unsigned)ceil_div(H, rlk::kBN);
   for (int c = 0; c <= last_split; ++c) {
     const int valid = (int)std::min<int64_t>(gg.S, V - (int64_t)c * gg.S);
-    hipLaunchKernelGGL(rlk::dz_tile, dim3(row_tiles, (unsigned)gg.cps), dim3(rlk::kThreads), 0, st, hb, Wb, y, idx,
-                       n_act, lse, g, (int)H, gm, c, (int)L.T_pad, (int)gg.S_pad, dZ, dZT);
-    RLK_TRY(launched("dz_tile"));
+    RLK_LAUNCH(dz_tile, dim3(row_tiles, (unsigned)gg.cps), dim3(rlk::kThreads), st, hb, Wb, y, idx, n_act, lse, g,
+               (int)H, gm, c, (int)L.T_pad, (int)gg.S_pad, dZ, dZT);
     if (grad_W) {
-      hipLaunchKernelGGL(rlk::grad_w_tile, dim3((unsigned)gg.cps, h_tiles), dim3(rlk::kThreads), 0, st, dZT, hT,
-                         n_act, (int)H, (int)L.T_pad, valid, (size_t)c * gg.S, grad_W);
-      RLK_TRY(launched("grad_w_tile"));
+      RLK_LAUNCH(grad_w_tile, dim3((unsigned)gg.cps, h_tiles), dim3(rlk::kThreads), st, dZT, hT, n_act, (int)H,
+                 (int)L.T_pad, valid, (size_t)c * gg.S, grad_W);
     }
     if (grad_h) {
-      hipLaunchKernelGGL(rlk::grad_h_tile, dim3(row_tiles, h_tiles), dim3(rlk::kThreads), 0, st, dZ,
-                         WT + (size_t)c * H * gg.S_pad, idx, n_act, (int)H, (int)gg.S_pad, c == 0 ? 1 : 0,
-                         c == last_split ? 1 : 0, ghacc, static_cast<uint16_t*>(grad_h));
-      RLK_TRY(launched("grad_h_tile"));
+      RLK_LAUNCH(grad_h_tile, dim3(row_tiles, h_tiles), dim3(rlk::kThreads), st, dZ, WT + (size_t)c * H * gg.S_pad,
+                 idx, n_act, (int)H, (int)gg.S_pad, c == 0 ? 1 : 0, c == last_split ? 1 : 0, ghacc,
+                 static_cast<uint16_t*>(grad_h));
     }
   }
   return ok();
+}
+
+rlk_status rlk_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  g_prof_on = true;
+  return ok();
+}
+
+rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t* n_entries) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = false;
+  std::vector<rlk_kernel_time_t> acc;
+  rlk_status st = RLK_OK;
+  for (auto& r : g_prof_recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == RLK_OK) st = fail(RLK_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+    size_t k = 0;
+    while (k < acc.size() && std::strcmp(acc[k].name, r.name) != 0) ++k;
+    if (k == acc.size()) {
+      rlk_kernel_time_t t{};
+      std::snprintf(t.name, sizeof(t.name), "%s", r.name);
+      acc.push_back(t);
+    }
+    acc[k].launches += 1;
+    acc[k].total_ms += ms;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  if (n_entries) *n_entries = (int32_t)acc.size();
+  for (size_t k = 0; out && k < acc.size() && (int32_t)k < max_entries; ++k) out[k] = acc[k];
+  return st == RLK_OK ? ok() : st;
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(rlk.library_path)
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -76,9 +76,11 @@ def test_fwd_validation():
     assert fwd(lse=MISALIGNED) == BAD_ALIGN
     assert fwd(nbytes=100) == WS_SMALL
     assert b"need" in rlk.lib().rlk_last_error_message()
-    # T == 0: nothing to do, nothing launched
+    # T == 0: nothing to do, nothing launched; empty tensors may be NULL
     assert fwd(T=0, nbytes=rlk.workspace_bytes(0, 0, 256, 4096)) == OK
+    assert fwd(T=0, h=None, y=None, logp=None, lse=None, ws=None, nbytes=0) == OK
     assert rlk.lib().rlk_last_error_message() == b""
+    assert fwd(T=0, H=100) == BAD_SHAPE
 
 
 def bwd(h=FAKE, W=FAKE, y=FAKE, lse=FAKE, g=FAKE, T=64, H=256, V=4096, gh=FAKE, gW=FAKE, ws=FAKE,
@@ -121,6 +123,7 @@ def test_partial_range_alignment():
 def test_merge_validation():
     L = rlk.lib()
     assert L.rlk_lse_merge(None, 2, FAKE, 8, -100, FAKE, FAKE, None) == NULL_ARG
+    assert L.rlk_lse_merge(None, 2, None, 0, -100, None, None, None) == OK
     assert L.rlk_lse_merge(FAKE, 0, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ARG
     assert L.rlk_lse_merge(FAKE, 33, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ARG
     assert L.rlk_lse_merge(FAKE, 2, FAKE, -1, -100, FAKE, FAKE, None) == BAD_SHAPE
