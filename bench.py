@@ -41,14 +41,10 @@ WORKLOADS = {
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
 }
 
-# algorithmic MFMA FLOPs per launch, in units of 2*T_act*H, as a function of V
-# (the three backward kernels run once per vocabulary split)
-KERNEL_FLOP_COLS = {
-    "fwd_chunks": lambda V, nsplit: V,
-    "dz_tile": lambda V, nsplit: V / nsplit,
-    "grad_w_tile": lambda V, nsplit: V / nsplit,
-    "grad_h_tile": lambda V, nsplit: V / nsplit,
-}
+# Kernels that carry the operator's MFMA work.  Each performs 2*T_act*H*V
+# algorithmic FLOPs per step (forward logits; backward recompute; grad_W;
+# grad_h), spread over its launches in that step.
+GEMM_KERNELS = ("fwd_tiles", "dz_tiles", "gradw_tiles", "gradh_tiles")
 
 
 def source_digest():
@@ -170,15 +166,16 @@ def main():
 
     digest = source_digest()
     kernels = {}
+    per_step_flops = 2.0 * T_act * H * V
     for name, (n, tot) in sorted(kern.items(), key=lambda kv: -kv[1][1]):
         avg = tot / n
         d = {"launches_per_step": n / args.steps, "avg_ms": avg, "ms_per_step": tot / args.steps}
-        if name in KERNEL_FLOP_COLS:
-            fl = 2.0 * T_act * H * KERNEL_FLOP_COLS[name](V, 32)
-            d["tflops"] = fl / (avg * 1e-3) / 1e12
+        if name in GEMM_KERNELS:
+            d["flops_per_launch"] = per_step_flops / (n / args.steps)
+            d["tflops"] = d["flops_per_launch"] / (avg * 1e-3) / 1e12
         kernels[name] = d
-    dom = max((k for k in kernels if k in KERNEL_FLOP_COLS), key=lambda k: kernels[k]["ms_per_step"])
-    dom_fl = 2.0 * T_act * H * KERNEL_FLOP_COLS[dom](V, 32)
+    dom = max((k for k in kernels if k in GEMM_KERNELS), key=lambda k: kernels[k]["ms_per_step"])
+    dom_fl = kernels[dom]["flops_per_launch"]
     achieved = dom_fl / (kernels[dom]["avg_ms"] * 1e-3)
     roofline = {
         "bound": "mfma",

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -79,30 +80,44 @@ FwdWs fwd_layout(int64_t T, int64_t V) {
   return w;
 }
 
+// Splits per backward group: the largest power of two G <= 32 whose dz
+// block (T_pad x G x S_pad bf16) fits the budget (default 1.25 GiB, env
+// RLK_DZ_BUDGET_MB overrides it).  G changes no result bit, only the
+// workspace size and the number of launches.
+int64_t dz_budget_bytes() {
+  const char* e = std::getenv("RLK_DZ_BUDGET_MB");
+  if (e && *e) {
+    const long long mb = std::atoll(e);
+    if (mb > 0) return (int64_t)mb << 20;
+  }
+  return (int64_t)1280 << 20;
+}
+
 struct BwdWs {
-  size_t idx, n_act, hT, WT, dZ, dZT, ghacc, total;
-  int64_t T_pad;
+  size_t idx, n_act, hA, dZ, ghacc, total;
+  int64_t T_pad, S_pad, G;
 };
 
 BwdWs bwd_layout(int64_t T, int64_t H, int64_t V) {
   const Geom g = geom_of(V);
   BwdWs w;
-  w.T_pad = ceil_div(T, rlk::kBM) * rlk::kBM;
+  w.T_pad = ceil_div(std::max<int64_t>(T, 1), rlk::kBM) * rlk::kBM;
+  w.S_pad = ceil_div(g.S, 64) * 64;
+  const int64_t per_split = 2 * w.T_pad * w.S_pad;
+  const int64_t budget = dz_budget_bytes();
+  w.G = 1;
+  while (w.G < rlk::kNSplit && 2 * w.G * per_split <= budget) w.G *= 2;
   size_t off = 0;
   w.idx = off;
   off = align256(off + sizeof(int32_t) * T);
   w.n_act = off;
   off = align256(off + sizeof(int32_t));
-  w.hT = off;
-  off = align256(off + 2 * (size_t)H * w.T_pad);
-  w.WT = off;
-  off = align256(off + 2 * (size_t)rlk::kNSplit * H * g.S_pad);
+  w.hA = off;
+  off = align256(off + 2 * (size_t)w.T_pad * H);
   w.dZ = off;
-  off = align256(off + 2 * (size_t)w.T_pad * g.S_pad);
-  w.dZT = off;
-  off = align256(off + 2 * (size_t)g.S_pad * w.T_pad);
+  off = align256(off + (size_t)per_split * w.G);
   w.ghacc = off;
-  off = align256(off + 4 * (size_t)T * H);
+  if (w.G < rlk::kNSplit) off = align256(off + 4 * (size_t)T * H);
   w.total = off;
   return w;
 }
@@ -244,10 +259,23 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   gm.cps = (int)g.cps;
   gm.s0 = s0;
   gm.vocab_start = (int)vocab_start;
-  const int64_t nchunks = (int64_t)nsplit * g.cps;
-  dim3 grid((unsigned)ceil_div(T, rlk::kBM), (unsigned)nchunks);
-  RLK_LAUNCH(fwd_chunks, grid, dim3(rlk::kThreads), st, static_cast<const uint16_t*>(h),
-             static_cast<const uint16_t*>(W), y, idx, n_act, (int)H, gm, (size_t)T, rec, zt);
+  rlk::FwdArgs fa;
+  fa.h = static_cast<const uint16_t*>(h);
+  fa.W = static_cast<const uint16_t*>(W);
+  fa.y = y;
+  fa.idx = idx;
+  fa.n_act = n_act;
+  fa.H = (int)H;
+  fa.nsplit = nsplit;
+  fa.gm = gm;
+  fa.tg.tps = (int)ceil_div(g.S, rlk::kBN);
+  fa.tg.row_tiles = (int)ceil_div(T, rlk::kBM);
+  const int64_t ntiles = (int64_t)fa.tg.row_tiles * nsplit * fa.tg.tps;
+  fa.tg.per = (int)ceil_div(ntiles, 8);
+  fa.rec_stride = (size_t)T;
+  fa.rec = rec;
+  fa.zt = zt;
+  RLK_LAUNCH(fwd_tiles, dim3((unsigned)(8 * fa.tg.per)), dim3(rlk::kThreads), st, fa);
 
   RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
              nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
@@ -353,22 +381,15 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   char* base = static_cast<char*>(ws);
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
   int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.hT);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(base + L.WT);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(base + L.dZ);
-  uint16_t* dZT = reinterpret_cast<uint16_t*>(base + L.dZT);
+  uint16_t* hA = reinterpret_cast<uint16_t*>(base + L.hA);
   float* ghacc = reinterpret_cast<float*>(base + L.ghacc);
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, n_act, nullptr, nullptr, nullptr);
-  if (grad_W) {
-    RLK_LAUNCH(transpose_h, dim3((unsigned)(L.T_pad / 64), (unsigned)(H / 64)), dim3(256), st, hb, idx, n_act,
-               (int)H, (int)L.T_pad, hT);
-  }
+  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, hA);
   if (grad_h) {
-    RLK_LAUNCH(transpose_w, dim3((unsigned)(gg.S_pad / 64), (unsigned)(H / 64), rlk::kNSplit), dim3(256), st, Wb,
-               (int)V, (int)H, (int)gg.S, (int)gg.S_pad, WT);
     RLK_LAUNCH(zero_rows, dim3((unsigned)T), dim3(256), st, y, ignore_index, (int)H, static_cast<uint16_t*>(grad_h));
   }
   rlk::SplitGeom gm;
@@ -380,20 +401,67 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   int last_split = 0;
   for (int c = 0; c < rlk::kNSplit; ++c)
     if ((int64_t)c * gg.S < V) last_split = c;
-  const unsigned row_tiles = (unsigned)ceil_div(T, rlk::kBM);
-  const unsigned h_tiles = (unsigned)ceil_div(H, rlk::kBN);
-  for (int c = 0; c <= last_split; ++c) {
-    const int valid = (int)std::min<int64_t>(gg.S, V - (int64_t)c * gg.S);
-    RLK_LAUNCH(dz_tile, dim3(row_tiles, (unsigned)gg.cps), dim3(rlk::kThreads), st, hb, Wb, y, idx, n_act, lse, g,
-               (int)H, gm, c, (int)L.T_pad, (int)gg.S_pad, dZ, dZT);
+  const int tps = (int)ceil_div(gg.S, rlk::kBN);
+  const int row_tiles = (int)ceil_div(T, rlk::kBM);
+  const int n_tiles = (int)ceil_div(H, rlk::kBN);
+  const int G = (int)L.G;
+  for (int c_lo = 0; c_lo <= last_split; c_lo += G) {
+    rlk::BwdGeom bg;
+    bg.c_lo = c_lo;
+    bg.G = G;
+    bg.S_pad = (int)L.S_pad;
+    bg.ldz = (int)(G * L.S_pad);
+    bg.T_pad = (int)L.T_pad;
+
+    rlk::DzArgs da;
+    da.hA = hA;
+    da.W = Wb;
+    da.y = y;
+    da.idx = idx;
+    da.n_act = n_act;
+    da.lse = lse;
+    da.g = g;
+    da.H = (int)H;
+    da.gm = gm;
+    da.tg.tps = tps;
+    da.tg.row_tiles = row_tiles;
+    da.tg.per = (int)ceil_div((int64_t)row_tiles * G * tps, 8);
+    da.bg = bg;
+    da.dZ = dZ;
+    RLK_LAUNCH(dz_tiles, dim3((unsigned)(8 * da.tg.per)), dim3(rlk::kThreads), st, da);
+
     if (grad_W) {
-      RLK_LAUNCH(grad_w_tile, dim3((unsigned)gg.cps, h_tiles), dim3(rlk::kThreads), st, dZT, hT, n_act, (int)H,
-                 (int)L.T_pad, valid, (size_t)c * gg.S, grad_W);
+      rlk::GradWArgs wa;
+      wa.dZ = dZ;
+      wa.hA = hA;
+      wa.idx = idx;
+      wa.n_act = n_act;
+      wa.H = (int)H;
+      wa.gm = gm;
+      wa.bg = bg;
+      wa.tps = tps;
+      wa.n_tiles = n_tiles;
+      wa.per = (int)ceil_div((int64_t)n_tiles * G * tps, 8);
+      wa.grad_W = grad_W;
+      RLK_LAUNCH(gradw_tiles, dim3((unsigned)(8 * wa.per)), dim3(rlk::kThreads), st, wa);
     }
     if (grad_h) {
-      RLK_LAUNCH(grad_h_tile, dim3(row_tiles, h_tiles), dim3(rlk::kThreads), st, dZ, WT + (size_t)c * H * gg.S_pad,
-                 idx, n_act, (int)H, (int)gg.S_pad, c == 0 ? 1 : 0, c == last_split ? 1 : 0, ghacc,
-                 static_cast<uint16_t*>(grad_h));
+      rlk::GradHArgs ha;
+      ha.dZ = dZ;
+      ha.W = Wb;
+      ha.idx = idx;
+      ha.n_act = n_act;
+      ha.H = (int)H;
+      ha.gm = gm;
+      ha.bg = bg;
+      ha.n_tiles = n_tiles;
+      ha.row_tiles = row_tiles;
+      ha.per = (int)ceil_div((int64_t)n_tiles * row_tiles, 8);
+      ha.first = c_lo == 0;
+      ha.last = c_lo + G > last_split;
+      ha.ghacc = ghacc;
+      ha.grad_h = static_cast<uint16_t*>(grad_h);
+      RLK_LAUNCH(gradh_tiles, dim3((unsigned)(8 * ha.per)), dim3(rlk::kThreads), st, ha);
     }
   }
   return ok();

@@ -2,19 +2,17 @@
 //
 // Forward / range partial:
 //   compact_rows       order-preserving list of active rows (target != ignore)
-//   fwd_chunks         MFMA logit tile + per-(row, chunk) statistics + target logit
+//   fwd_tiles          MFMA logit tiles + per-(row, chunk) statistics + target logit
 //   merge_splits       chunk fold per split, pairwise tree over splits, epilogue
 //   merge_parts        tree over per-range statistics (rlk_lse_merge)
-// Backward (per vocabulary split c, ascending):
-//   transpose_h        hT[k][i] = h[row_i][k] for the active rows, zero padded
-//   transpose_w        WT[c][k][j] = W[c*S + j][k], zero padded
-//   dz_tile            recomputed logits -> dz = g (onehot - softmax), bf16
-//   grad_w_tile        grad_W rows of split c = dz_c^T h  (K = active rows)
-//   grad_h_tile        fp32 accumulator += dz_c W_c; bf16 after the last split
+// Backward (per group of vocabulary splits, ascending):
+//   dz_tiles           recomputed logits -> dz = g (onehot - softmax), bf16
+//   gradw_tiles        grad_W rows of the group = dz^T h  (K = active rows)
+//   gradh_tiles        fp32 accumulator += dz W; bf16 after the last group
 //   zero_rows          zero grad_h rows of inactive rows
 #pragma once
 
-#include "rlk_device.h"
+#include "rlk_gemm.h"
 
 namespace rlk {
 
@@ -65,19 +63,7 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Forward chunk statistics.
-// grid.x: 128-row tiles of the active rows; grid.y: chunk g of the processed
-// split range (split = s0 + g / cps, chunk j = g % cps).  Writes
-// rec[g * rec_stride + i] = (m, s) of chunk g for active row i, and zt[i] =
-// logit of the target for the one chunk that holds it.
-//
-// Chunk statistics, for one row over the chunk's valid columns
-// c = 32 b + q (b = 0..3 column block, q = 0..31 lane):
-//   m = max_c z_c (exact);
-//   e_c = exp(z_c - m), 0 for invalid columns;
-//   a_q = ((e_q + e_{32+q}) + e_{64+q}) + e_{96+q};
-//   s = pairwise tree over q = 0..31 of a_q (xor butterfly; every lane ends
-//       with the same value because fp addition is commutative).
+// Vocabulary geometry
 // ---------------------------------------------------------------------------
 struct SplitGeom {
   int V;           // global vocabulary size
@@ -98,83 +84,131 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
 __device__ __forceinline__ float xor_max(float v, int d) { return fmaxf(v, __shfl_xor(v, d, 64)); }
 __device__ __forceinline__ float xor_add(float v, int d) { return v + __shfl_xor(v, d, 64); }
 
-__global__ __launch_bounds__(kThreads) void fwd_chunks(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                       const int32_t* __restrict__ y, const int32_t* __restrict__ idx,
-                                                       const int32_t* __restrict__ n_act_p, int H, SplitGeom gm,
-                                                       size_t rec_stride, float2* __restrict__ rec,
-                                                       float* __restrict__ zt) {
-  __shared__ uint4 lds[4 * kLdsStage];
-  const int n_act = *n_act_p;
-  const int i0 = blockIdx.x * kBM;
+// ---------------------------------------------------------------------------
+// Forward chunk statistics on 256 x 256 tiles.
+//
+// Tile (rt, ct): active rows [256 rt, +256) x columns [c0, c0 + 256) of one
+// split, c0 = split start + 256 j; wave (wm, wn) holds the 128-column chunk
+// 2j + wn of that split.  Writes rec[g * rec_stride + i] = (m, s) of chunk g
+// (g = local split * cps + chunk) for active row i, and zt[i] = the target's
+// logit, written by the one chunk that holds it.
+//
+// Chunk statistics of one row over the chunk's valid columns
+// c = 32 b + q (b = 0..3 MFMA column block, q = 0..31 lane):
+//   m = max_c z_c (exact);
+//   e_c = exp(z_c - m), 0 for invalid columns;
+//   a_q = ((e_q + e_{32+q}) + e_{64+q}) + e_{96+q};
+//   s = pairwise tree over q = 0..31 of a_q (xor butterfly; every lane ends
+//       with the same value because fp addition is commutative).
+// ---------------------------------------------------------------------------
+struct TileGeom {
+  int tps;        // 256-column tiles per split = ceil(S / 256)
+  int row_tiles;  // 256-row tiles covering T
+  int per;        // tiles per XCD (grid = 8 * per)
+};
+
+struct FwdArgs {
+  const uint16_t* h;
+  const uint16_t* W;
+  const int32_t* y;
+  const int32_t* idx;
+  const int32_t* n_act;
+  int H;
+  int nsplit;
+  SplitGeom gm;
+  TileGeom tg;
+  size_t rec_stride;
+  float2* rec;
+  float* zt;
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_tiles(FwdArgs a) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int id = xcd_tile(a.tg.per);
+  if (id >= a.tg.row_tiles * a.nsplit * a.tg.tps) return;
+  const int ct = id / a.tg.row_tiles, rt = id - ct * a.tg.row_tiles;
+  const int n_act = *a.n_act;
+  const int i0 = rt * kBM;
   if (i0 >= n_act) return;
-  const int g = blockIdx.y;
-  int c0, c1;
-  chunk_cols(gm, g, c0, c1);
-  if (c0 >= c1) return;
+  const int sl = ct / a.tg.tps, j = ct - sl * a.tg.tps;
+  const int sbeg = (a.gm.s0 + sl) * a.gm.S;
+  const int send = min(sbeg + a.gm.S, a.gm.V);
+  const int c0 = sbeg + j * kBN;
+  if (c0 >= send) return;
+  const int c1 = min(c0 + kBN, send);
 
   const int tid = threadIdx.x;
-  const int r0 = tid >> 3;
-  const int ia0 = idx[min(i0 + r0, n_act - 1)], ia1 = idx[min(i0 + r0 + 32, n_act - 1)];
-  const int ia2 = idx[min(i0 + r0 + 64, n_act - 1)], ia3 = idx[min(i0 + r0 + 96, n_act - 1)];
-  const int wb = c1 - 1 - gm.vocab_start, cb = c0 - gm.vocab_start;
-  const TileRows R{h + (size_t)ia0 * H, h + (size_t)ia1 * H, h + (size_t)ia2 * H, h + (size_t)ia3 * H,
-                   W + (size_t)min(cb + r0, wb) * H, W + (size_t)min(cb + r0 + 32, wb) * H,
-                   W + (size_t)min(cb + r0 + 64, wb) * H, W + (size_t)min(cb + r0 + 96, wb) * H};
-  f32x16 acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
-  gemm_tile(R, H / kBK, acc, lds);
+  const RowsK8 A = rows_k_gather(a.h, a.idx, i0, n_act - 1, a.H);
+  const RowsK8 B = rows_k_strided(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
+  Acc acc;
+  acc_zero(acc);
+  gemm256<false, false>(A, B, a.H / kBK, acc, lds);
 
   // targets of the tile's rows, staged in LDS (the main loop ended with a barrier)
   int* ys = reinterpret_cast<int*>(lds);
   if (tid < kBM) {
     const int i = i0 + tid;
-    ys[tid] = (i < n_act) ? y[idx[i]] : -1;
+    ys[tid] = (i < n_act) ? a.y[a.idx[i]] : -1;
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6, q = lane & 31;
-  const int width = c1 - c0;
+  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  const int cc0 = c0 + kChunk * wn;  // this wave's chunk
+  const int width = min(cc0 + kChunk, c1) - cc0;
+  if (width <= 0) return;
+  const int g = sl * a.gm.cps + 2 * j + wn;
   bool valid[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) valid[b] = (32 * b + q) < width;
 
-  float keep_m = 0.f, keep_s = 0.f;
+  float keep_m[kMI] = {}, keep_s[kMI] = {};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float mx = -INFINITY;
+  for (int mi = 0; mi < kMI; ++mi) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (valid[b]) mx = fmaxf(mx, acc[b][r]);
-    mx = xor_max(mx, 1);
-    mx = xor_max(mx, 2);
-    mx = xor_max(mx, 4);
-    mx = xor_max(mx, 8);
-    mx = xor_max(mx, 16);
-    float e[4];
+    for (int rr = 0; rr < 16; ++rr) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) e[b] = valid[b] ? rlk_exp(acc[b][r] - mx) : 0.f;
-    float a = ((e[0] + e[1]) + e[2]) + e[3];
-    a = xor_add(a, 1);
-    a = xor_add(a, 2);
-    a = xor_add(a, 4);
-    a = xor_add(a, 8);
-    a = xor_add(a, 16);
-    if (q == r) {
-      keep_m = mx;
-      keep_s = a;
+      for (int b = 0; b < 4; ++b)
+        if (valid[b]) mx = fmaxf(mx, acc.c[mi][b][rr]);
+      mx = xor_max(mx, 1);
+      mx = xor_max(mx, 2);
+      mx = xor_max(mx, 4);
+      mx = xor_max(mx, 8);
+      mx = xor_max(mx, 16);
+      float e[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) e[b] = valid[b] ? rlk_exp(acc.c[mi][b][rr] - mx) : 0.f;
+      float s = ((e[0] + e[1]) + e[2]) + e[3];
+      s = xor_add(s, 1);
+      s = xor_add(s, 2);
+      s = xor_add(s, 4);
+      s = xor_add(s, 8);
+      s = xor_add(s, 16);
+      if (q == rr) {
+        keep_m[mi] = mx;
+        keep_s[mi] = s;
+      }
+      const int row = acc_row(wm, mi, rr, lane);
+      const int tc = ys[row] - cc0;
+      if (tc >= 0 && tc < width && (tc & 31) == q) {
+        const int b = tc >> 5;
+        float v = acc.c[mi][0][rr];
+        v = (b == 1) ? acc.c[mi][1][rr] : v;
+        v = (b == 2) ? acc.c[mi][2][rr] : v;
+        v = (b == 3) ? acc.c[mi][3][rr] : v;
+        a.zt[i0 + row] = v;
+      }
     }
-    // target logit: the lane holding column (y - c0) of this row
-    const int row = wave * 32 + acc_row(r, lane);
-    const int tc = ys[row] - c0;
-    if (tc >= 0 && tc < width && (tc & 31) == q) zt[i0 + row] = acc_get(acc, tc >> 5, r);
   }
   if (q < 16) {
-    const int row = wave * 32 + acc_row(q, lane);
-    const int i = i0 + row;
-    if (i < n_act) rec[(size_t)g * rec_stride + i] = make_float2(keep_m, keep_s);
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int i = i0 + acc_row(wm, mi, q, lane);
+      if (i < n_act) a.rec[(size_t)g * a.rec_stride + i] = make_float2(keep_m[mi], keep_s[mi]);
+    }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // Split fold + tree + epilogue.  grid.x: 64 active rows per block; 8 waves,
@@ -288,206 +322,280 @@ __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Backward helpers
+// Backward.  The vocabulary splits are processed in groups of G consecutive
+// splits [c_lo, c_lo + G); dz of a group lives in the workspace as
+// dZ[t][sc * S_pad + v] (bf16, t = active-row index, sc = split within the
+// group, v = column within the split, S_pad = S rounded up to 64, zero
+// padded).  The grouping changes no result bit: grad_W's chain runs over
+// rows and grad_h's chain runs over the vocabulary in ascending order with
+// the same zero padding after every split, whatever G is.
 // ---------------------------------------------------------------------------
+struct BwdGeom {
+  int c_lo;   // first split of the group
+  int G;      // splits in the group
+  int S_pad;  // S rounded up to 64
+  int ldz;    // G * S_pad
+  int T_pad;  // rows of dZ (multiple of 256)
+};
 
-// hT[k * ldt + i] = h[idx[i] * H + k] for i < n_act, 0 for n_act <= i < ldt.
-// grid (ldt / 64, H / 64), block 256; 64x64 tile through LDS.
-__global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
-                                                   const int32_t* __restrict__ n_act_p, int H, int ldt,
-                                                   uint16_t* __restrict__ hT) {
-  __shared__ uint16_t tile[64][65];
-  const int n_act = *n_act_p;
-  const int i0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int i = i0 + r;
-    tile[r][tx] = (i < n_act) ? h[(size_t)idx[i] * H + k0 + tx] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int r = ty; r < 64; r += 4) hT[(size_t)(k0 + r) * ldt + i0 + tx] = tile[tx][r];
-}
+struct DzArgs {
+  const uint16_t* hA;  // active rows of h, compacted, zero padded to T_pad
+  const uint16_t* W;
+  const int32_t* y;
+  const int32_t* idx;
+  const int32_t* n_act;
+  const float* lse;
+  const float* g;
+  int H;
+  SplitGeom gm;
+  TileGeom tg;
+  BwdGeom bg;
+  uint16_t* dZ;
+};
 
-// WT[(c * H + k) * S_pad + j] = W[(c * S + j) * H + k] for j < valid(c), else 0.
-// grid (S_pad / 64, H / 64, 32), block 256.
-__global__ __launch_bounds__(256) void transpose_w(const uint16_t* __restrict__ W, int V, int H, int S, int S_pad,
-                                                   uint16_t* __restrict__ WT) {
-  __shared__ uint16_t tile[64][65];
-  const int c = blockIdx.z;
-  const int j0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
-  const int valid = max(0, min(S, V - c * S));
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int j = j0 + r;
-    tile[r][tx] = (j < valid) ? W[(size_t)(c * S + j) * H + k0 + tx] : (uint16_t)0;
-  }
-  __syncthreads();
-  uint16_t* dst = WT + (size_t)c * H * S_pad;
-  for (int r = ty; r < 64; r += 4) dst[(size_t)(k0 + r) * S_pad + j0 + tx] = tile[tx][r];
-}
-
-// dz for split c: grid (row tiles, cps).  For active row i and column v of the
-// split:  p = exp(z - lse_i),  dz = g_i * ([v == y_i] - p)  in fp32, then
-// rounded to bf16 (RNE).  Written as dZ[i][v_local] (ld S_pad) and
-// dZT[v_local][i] (ld T_pad); rows >= n_act and invalid columns get 0.
-__global__ __launch_bounds__(kThreads) void dz_tile(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                                                    const int32_t* __restrict__ y, const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ n_act_p, const float* __restrict__ lse,
-                                                    const float* __restrict__ gup, int H, SplitGeom gm, int split,
-                                                    int T_pad, int S_pad, uint16_t* __restrict__ dZ,
-                                                    uint16_t* __restrict__ dZT) {
-  __shared__ uint4 lds[4 * kLdsStage];
-  const int n_act = *n_act_p;
-  const int i0 = blockIdx.x * kBM;
+// dz for the group's splits on 256 x 256 tiles (same tiles and logits as the
+// forward): p = exp(z - lse_i), dz = g_i * ([v == y_i] - p) in fp32, rounded
+// once to bf16.  Rows >= n_act of the tile and columns >= the split's width
+// are written as zeros.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dz_tiles(DzArgs a) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int id = xcd_tile(a.tg.per);
+  if (id >= a.tg.row_tiles * a.bg.G * a.tg.tps) return;
+  const int ct = id / a.tg.row_tiles, rt = id - ct * a.tg.row_tiles;
+  const int n_act = *a.n_act;
+  const int i0 = rt * kBM;
   if (i0 >= n_act) return;
-  const int j = blockIdx.y;
-  const int sstart = split * gm.S;
-  const int send = min(sstart + gm.S, gm.V);
-  const int c0 = sstart + j * kChunk;
-  const int c1 = min(c0 + kChunk, send);
-  const int width = max(0, c1 - c0);
+  const int sc = ct / a.tg.tps, j = ct - sc * a.tg.tps;
+  const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
+  const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));  // columns of this split
+  const int c0 = sbeg + j * kBN;
+  const int c1 = sbeg + min(j * kBN + kBN, valid_s);
   const int tid = threadIdx.x;
-  f32x16 acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
-  if (width > 0) {
-    const int r0 = tid >> 3;
-    const int ia0 = idx[min(i0 + r0, n_act - 1)], ia1 = idx[min(i0 + r0 + 32, n_act - 1)];
-    const int ia2 = idx[min(i0 + r0 + 64, n_act - 1)], ia3 = idx[min(i0 + r0 + 96, n_act - 1)];
-    const int wb = c1 - 1;
-    const TileRows R{h + (size_t)ia0 * H, h + (size_t)ia1 * H, h + (size_t)ia2 * H, h + (size_t)ia3 * H,
-                     W + (size_t)min(c0 + r0, wb) * H, W + (size_t)min(c0 + r0 + 32, wb) * H,
-                     W + (size_t)min(c0 + r0 + 64, wb) * H, W + (size_t)min(c0 + r0 + 96, wb) * H};
-    gemm_tile(R, H / kBK, acc, lds);
+  Acc acc;
+  acc_zero(acc);
+  if (c0 < c1) {
+    const RowsK8 A = rows_k_strided(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
+    const RowsK8 B = rows_k_strided(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
+    gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
-  float* rowv = reinterpret_cast<float*>(lds);  // [128] lse, [128] g, [128] y
+  float* rv = reinterpret_cast<float*>(lds);  // [256] lse, [256] g, [256] y
+  int* ry = reinterpret_cast<int*>(lds) + 2 * kBM;
   if (tid < kBM) {
     const int i = i0 + tid;
     if (i < n_act) {
-      const int t = idx[i];
-      rowv[tid] = lse[t];
-      rowv[128 + tid] = gup[t];
-      reinterpret_cast<int*>(rowv)[256 + tid] = y[t];
+      const int t = a.idx[i];
+      rv[tid] = a.lse[t];
+      rv[kBM + tid] = a.g[t];
+      ry[tid] = a.y[t];
     } else {
-      rowv[tid] = 0.f;
-      rowv[128 + tid] = 0.f;
-      reinterpret_cast<int*>(rowv)[256 + tid] = -1;
+      rv[tid] = 0.f;
+      rv[kBM + tid] = 0.f;
+      ry[tid] = -1;
     }
   }
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6, q = lane & 31;
-  const int vbase = j * kChunk;  // split-local column of the chunk start
+  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int cl = 32 * b + q;  // chunk-local column
-    const bool cvalid = cl < width;
+    const int vl = j * kBN + kChunk * wn + 32 * b + q;  // column within the split
+    if (vl >= a.bg.S_pad) continue;
+    const bool cvalid = vl < valid_s;
+    const int v = sbeg + vl;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      uint16_t o[4];
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = 4 * r4 + rr;
-        const int row = wave * 32 + acc_row(r, lane);
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = acc_row(wm, mi, rr, lane);
         const int i = i0 + row;
         float d = 0.f;
         if (cvalid && i < n_act) {
-          const float p = rlk_exp(acc[b][r] - rowv[row]);
-          const float delta = (reinterpret_cast<const int*>(rowv)[256 + row] == c0 + cl) ? 1.f : 0.f;
-          d = rowv[128 + row] * (delta - p);
+          const float p = rlk_exp(acc.c[mi][b][rr] - rv[row]);
+          const float delta = (ry[row] == v) ? 1.f : 0.f;
+          d = rv[kBM + row] * (delta - p);
         }
-        o[rr] = f32_to_bf16_rne(d);
-        dZ[(size_t)i * S_pad + vbase + cl] = o[rr];
+        dzs[(size_t)i * a.bg.ldz + vl] = f32_to_bf16_rne(d);
       }
-      // rows 8*r4 + 4*(lane>>5) + 0..3 are consecutive: one 8-byte store into dZT
-      const int row0 = wave * 32 + acc_row(4 * r4, lane);
-      uint2 pk;
-      pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-      pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-      *reinterpret_cast<uint2*>(dZT + (size_t)(vbase + cl) * T_pad + i0 + row0) = pk;
-    }
   }
 }
 
-// grad_W rows of split c: C[v][n] = sum_i dZT[v][i] hT[n][i], K = active rows
-// rounded up to 64 (the padding rows of dZT and hT are zero).  grid
-// (S_pad / 128, ceil(H / 128)).  Written once, fp32.
-__global__ __launch_bounds__(kThreads) void grad_w_tile(const uint16_t* __restrict__ dZT,
-                                                        const uint16_t* __restrict__ hT,
-                                                        const int32_t* __restrict__ n_act_p, int H, int T_pad,
-                                                        int valid_rows, size_t out_row0, float* __restrict__ grad_W) {
-  __shared__ uint4 lds[4 * kLdsStage];
-  const int n_act = *n_act_p;
-  const int v0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
-  if (v0 >= valid_rows) return;
+// MN-mode loader over a row-major matrix: k-row t of k-block kt is matrix
+// row 64 kt + t at this tile's columns (dz columns for grad_W's A operand,
+// compacted hidden rows for its B operand).
+struct ColsMN {
+  const uint16_t* col[8];  // matrix + column of piece i (row 0)
+  int ld;
+  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(col[i] + (size_t)(kt * kBK + dma_mn_krow(i)) * ld, tile, dma_slot0(i));
+  }
+};
+
+// MN-mode loader over the group's vocabulary rows of W: k index kg of the
+// group -> split sc = kg / S_pad, row (c_lo + sc) * S + kg % S_pad (clamped
+// to V - 1; those rows meet dz = 0).
+struct WRowsMN {
+  const uint16_t* col[8];  // W + column of piece i
+  int H, S, S_pad, c_lo, V;
+  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+    const int kg = kt * kBK;
+    const int sc = kg / S_pad;
+    const int base = (c_lo + sc) * S + (kg - sc * S_pad);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma16(col[i] + (size_t)min(base + dma_mn_krow(i), V - 1) * H, tile, dma_slot0(i));
+  }
+};
+
+struct GradWArgs {
+  const uint16_t* dZ;
+  const uint16_t* hA;  // active rows of h, compacted, zero padded to T_pad
+  const int32_t* idx;
+  const int32_t* n_act;
+  int H;
+  SplitGeom gm;
+  BwdGeom bg;
+  int tps;      // 256-row v tiles per split
+  int n_tiles;  // 256-column tiles of H
+  int per;
+  float* grad_W;
+};
+
+// grad_W rows of the group's splits: C[v][n] = sum_t dz[t][v] h[t][n], the
+// chain over active rows t ascending (K padded to 64 with zero dz rows).
+// Both operands are MN mode.  Written once, fp32.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gradw_tiles(GradWArgs a) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int id = xcd_tile(a.per);
+  if (id >= a.n_tiles * a.bg.G * a.tps) return;
+  const int vt = id / a.n_tiles, nt = id - vt * a.n_tiles;
+  const int sc = vt / a.tps, j = vt - sc * a.tps;
+  const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
+  const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));
+  const int v0 = j * kBM;  // within the split
+  if (v0 >= valid_s) return;
+  const int n0 = nt * kBN;
+  const int n_act = *a.n_act;
   const int tid = threadIdx.x;
-  const int r0 = tid >> 3;
-  const TileRows R{dZT + (size_t)(v0 + r0) * T_pad, dZT + (size_t)(v0 + r0 + 32) * T_pad,
-                   dZT + (size_t)(v0 + r0 + 64) * T_pad, dZT + (size_t)(v0 + r0 + 96) * T_pad,
-                   hT + (size_t)min(n0 + r0, H - 1) * T_pad, hT + (size_t)min(n0 + r0 + 32, H - 1) * T_pad,
-                   hT + (size_t)min(n0 + r0 + 64, H - 1) * T_pad, hT + (size_t)min(n0 + r0 + 96, H - 1) * T_pad};
-  f32x16 acc[4];
+  ColsMN A, B;
+  A.ld = a.bg.ldz;
+  B.ld = a.H;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
-  gemm_tile(R, (n_act + kBK - 1) / kBK, acc, lds);
-  const int lane = tid & 63, wave = tid >> 6, q = lane & 31;
+  for (int i = 0; i < 8; ++i) {
+    const int p8 = dma_mn_piece(dma_mn_krow(i)) * 8;
+    A.col[i] = a.dZ + (size_t)sc * a.bg.S_pad + min(v0 + p8, a.bg.S_pad - 8);
+    B.col[i] = a.hA + min(n0 + p8, a.H - 8);
+  }
+  Acc acc;
+  acc_zero(acc);
+  gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
+  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  float* out = a.grad_W + (size_t)sbeg * a.H;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int n = n0 + 32 * b + q;
-    if (n >= H) continue;
+  for (int ni = 0; ni < 4; ++ni) {
+    const int n = n0 + 128 * wn + 32 * ni + q;
+    if (n >= a.H) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = v0 + wave * 32 + acc_row(r, lane);
-      if (v < valid_rows) grad_W[(out_row0 + v) * (size_t)H + n] = acc[b][r];
-    }
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int v = v0 + acc_row(wm, mi, rr, lane);
+        if (v < valid_s) out[(size_t)v * a.H + n] = acc.c[mi][ni][rr];
+      }
   }
 }
 
-// grad_h: acc[i][n] (+)= sum_v dZ[i][v] WT_c[n][v] over split c, K = S_pad
-// (zero padded).  The fp32 accumulator chain continues across splits through
-// ghacc (exact fp32 store/load), so grad_h is one chain over the vocabulary
-// in ascending order.  After the last split the result is rounded to bf16
-// once and written to the row's place in grad_h.  grid (row tiles, ceil(H/128)).
-__global__ __launch_bounds__(kThreads) void grad_h_tile(const uint16_t* __restrict__ dZ,
-                                                        const uint16_t* __restrict__ WTc,
-                                                        const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ n_act_p, int H, int S_pad,
-                                                        int first, int last, float* __restrict__ ghacc,
-                                                        uint16_t* __restrict__ grad_h) {
-  __shared__ uint4 lds[4 * kLdsStage];
-  const int n_act = *n_act_p;
-  const int i0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;
+struct GradHArgs {
+  const uint16_t* dZ;
+  const uint16_t* W;
+  const int32_t* idx;
+  const int32_t* n_act;
+  int H;
+  SplitGeom gm;
+  BwdGeom bg;
+  int n_tiles;    // 256-column tiles of H
+  int row_tiles;  // 256-row tiles covering T
+  int per;
+  int first, last;
+  float* ghacc;
+  uint16_t* grad_h;
+};
+
+// grad_h of the group: acc[i][n] (+)= sum_v dz[i][v] W[v][n] over the
+// group's padded columns.  A (dz rows) is K mode, B (W rows) MN mode.  The
+// fp32 chain continues across groups through ghacc (exact store/load); after
+// the last group it is rounded to bf16 once and written to the row's place.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gradh_tiles(GradHArgs a) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int id = xcd_tile(a.per);
+  if (id >= a.n_tiles * a.row_tiles) return;
+  const int rt = id / a.n_tiles, nt = id - rt * a.n_tiles;
+  const int n_act = *a.n_act;
+  const int i0 = rt * kBM, n0 = nt * kBN;
   if (i0 >= n_act) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, q = lane & 31;
-  f32x16 acc[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  Acc acc;
+  acc_zero(acc);
+  if (!a.first) {
+    // continue the chain from the previous groups (rows/columns outside
+    // the problem read a clamped, valid address; they are never stored)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int n = n0 + 32 * b + q;
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = min(n0 + 128 * wn + 32 * ni + q, a.H - 1);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + wave * 32 + acc_row(r, lane);
-      acc[b][r] = (!first && i < n_act && n < H) ? ghacc[(size_t)i * H + n] : 0.f;
+      for (int mi = 0; mi < kMI; ++mi) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int i = min(i0 + acc_row(wm, mi, rr, lane), n_act - 1);
+          acc.c[mi][ni][rr] = a.ghacc[(size_t)i * a.H + n];
+        }
+        // bound the loads in flight (each block lands in its accumulator)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
-  const int r0 = tid >> 3;
-  const TileRows R{dZ + (size_t)(i0 + r0) * S_pad, dZ + (size_t)(i0 + r0 + 32) * S_pad,
-                   dZ + (size_t)(i0 + r0 + 64) * S_pad, dZ + (size_t)(i0 + r0 + 96) * S_pad,
-                   WTc + (size_t)min(n0 + r0, H - 1) * S_pad, WTc + (size_t)min(n0 + r0 + 32, H - 1) * S_pad,
-                   WTc + (size_t)min(n0 + r0 + 64, H - 1) * S_pad, WTc + (size_t)min(n0 + r0 + 96, H - 1) * S_pad};
-  gemm_tile(R, S_pad / kBK, acc, lds);
+  const RowsK8 A = rows_k_strided(a.dZ + (size_t)i0 * a.bg.ldz, kBM - 1, a.bg.ldz);
+  WRowsMN B;
+  B.H = a.H;
+  B.S = a.gm.S;
+  B.S_pad = a.bg.S_pad;
+  B.c_lo = a.bg.c_lo;
+  B.V = a.gm.V;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int n = n0 + 32 * b + q;
-    if (n >= H) continue;
+  for (int i = 0; i < 8; ++i) B.col[i] = a.W + min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8);
+  gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + wave * 32 + acc_row(r, lane);
-      if (i >= n_act) continue;
-      if (last)
-        grad_h[(size_t)idx[i] * H + n] = f32_to_bf16_rne(acc[b][r]);
-      else
-        ghacc[(size_t)i * H + n] = acc[b][r];
-    }
+  for (int ni = 0; ni < 4; ++ni) {
+    const int n = n0 + 128 * wn + 32 * ni + q;
+    if (n >= a.H) continue;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int i = i0 + acc_row(wm, mi, rr, lane);
+        if (i >= n_act) continue;
+        if (a.last)
+          a.grad_h[(size_t)a.idx[i] * a.H + n] = f32_to_bf16_rne(acc.c[mi][ni][rr]);
+        else
+          a.ghacc[(size_t)i * a.H + n] = acc.c[mi][ni][rr];
+      }
+  }
+}
+
+
+// hA[i] = h[idx[i]] for active rows i < n_act, zero rows for n_act <= i <
+// rows.  grid rows, block 256; 16-byte pieces.
+__global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ n_act_p, int H,
+                                                   uint16_t* __restrict__ hA) {
+  const int i = blockIdx.x;
+  const int n_act = *n_act_p;
+  u32x4* dst = reinterpret_cast<u32x4*>(hA + (size_t)i * H);
+  if (i < n_act) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)idx[i] * H);
+    for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
+  } else {
+    for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 

@@ -49,8 +49,14 @@ def test_workspace_bytes():
     assert W(0, 4096, 4096, 151936) >= 32 * 38 * 4096 * 8
     assert W(2, 4096, 4096, 151936) == W(0, 4096, 4096, 151936)
     bwd = W(1, 4096, 4096, 151936)
-    # transposed weight copy (32 splits x H x padded split) dominates
-    assert bwd >= 2 * 32 * 4096 * 4864
+    # the dz block of all 32 splits (4800 padded columns each) fits the default
+    # budget; plus the compacted hidden rows
+    dz_all = 2 * 4096 * 32 * 4800
+    h_act = 2 * 4096 * 4096
+    assert dz_all + h_act <= bwd < dz_all + h_act + (1 << 20)
+    # at T = 16384 the default budget holds 8 splits, plus the fp32 grad_h accumulator
+    bwd3 = W(1, 16384, 2048, 151936)
+    assert bwd3 >= 2 * 16384 * 8 * 4800 + 4 * 16384 * 2048
     assert W(0, 0, 64, 10) > 0
     for bad in [(0, -1, 64, 10), (0, 4, 63, 10), (0, 4, 0, 10), (0, 4, 64, 0), (7, 4, 64, 10),
                 (0, 4, 64, 8_000_001)]:

@@ -125,3 +125,15 @@ def test_qwen3_8b_shape_fwd_bwd_sampled():
 
 def test_qwen3_30b_a3b_shape_fwd_bwd_sampled():
     _full_shape_check("qwen3_30b_a3b", n_rows=12, n_vocab=12)
+
+
+def test_split_grouping_changes_no_bit(monkeypatch):
+    # the backward processes the vocabulary in groups of splits sized by a
+    # workspace budget; any grouping must give the same bits
+    inp = synth.make_inputs(700, 256, 30000, 0.15)
+    (h, W, y, g), logp, lse, gh, gW = fwd_bwd(inp)
+    for mb in ("1", "4", "16"):
+        monkeypatch.setenv("RLK_DZ_BUDGET_MB", mb)
+        gh2, gW2 = rlk.linear_logp_bwd(h, W, y, lse, g)
+        torch.cuda.synchronize()
+        assert torch.equal(gh, gh2) and torch.equal(gW, gW2), mb
