@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/rlk.h"
+#include "rlk.h"
 #include "rlk_kernels.h"
 
 namespace {

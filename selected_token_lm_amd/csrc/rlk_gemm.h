@@ -31,8 +31,8 @@
 // Both LDS layouts are XOR-swizzled so that the 16 lanes served per LDS
 // cycle hit distinct banks.
 //
-// Double-buffered: while k-block kt is multiplied from one LDS stage, block
-// kt+1 is loaded straight from global memory into the other stage.
+// Pipelined: k-blocks of 32 are loaded straight from global memory into a
+// ring of four LDS stages, three k-blocks ahead of the MFMAs.
 #pragma once
 
 #include "rlk_device.h"
@@ -44,16 +44,20 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // registers in private memory)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 256;
 constexpr int kMI = 4, kNI = 4;            // 32 x 32 blocks per wave
-constexpr int kTileU4 = 2048;              // u32x4 per operand tile (32 KB)
+constexpr int kKK = kBK / 16;              // MFMA k steps per k-block
+constexpr int kSegs = kBK / 8;             // 16-byte pieces per K-mode row
+constexpr int kDma = kBK / 8;              // direct-load instructions per wave per operand per k-block
+constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (16 KB)
 constexpr int kStageU4 = 2 * kTileU4;      // A + B
-constexpr int kLdsU4 = 2 * kStageU4;       // two stages: 128 KB
+constexpr int kNS = 4;                     // LDS stages (k-blocks in the ring)
+constexpr int kLdsU4 = kNS * kStageU4;     // 128 KB
 
-// K-mode slot of (row, 16-byte piece seg): rows r and r+1 sit in opposite
-// 128-byte halves of a 256-byte bank row, and the piece index is xor-ed with
-// (row >> 1) so that 16 consecutive rows of one k piece cover all banks.
-__device__ __forceinline__ int slot_k(int row, int seg) { return row * 8 + (seg ^ ((row >> 1) & 7)); }
+// K-mode slot of (row, 16-byte piece seg), 64-byte rows: four consecutive
+// rows fill a 256-byte bank row and the piece index is xor-ed with
+// (row >> 2) & 3, so 16 consecutive rows of one k piece cover all banks.
+__device__ __forceinline__ int slot_k(int row, int seg) { return row * kSegs + (seg ^ ((row >> 2) & 3)); }
 
 // MN-mode slot of (k-row, 16-byte piece p of 32): 64-byte blocks of the row
 // xor-ed with (k-row & 7).
@@ -92,11 +96,12 @@ __device__ __forceinline__ bf16x8 frag_a(const u32x4* t, int r0, int kk, int lan
 // Tiles are filled with global_load_lds_dwordx4: one wave instruction loads
 // 64 x 16 bytes and writes them to 1 KB of LDS at its (wave-uniform) base,
 // lane l at byte 16 l.  Instruction i of wave w covers tile slots
-// 64 (8 w + i) .. +64, so lane l of it fills slot s = 64 (8 w + i) + l and
+// 64 (kDma w + i) .. +64, so lane l of it fills slot s = 64 (kDma w + i) + l and
 // fetches the global piece that the swizzled layout puts there:
-//   K mode : row 64 w + 8 i + (l >> 3), piece (l & 7) ^ ((row >> 1) & 7)
-//   MN mode: k-row 16 w + 2 i + (l >> 5),
+//   K mode : row 64 w + 16 i + (l >> 2), piece (l & 3) ^ ((row >> 2) & 3)
+//   MN mode: k-row 8 w + 2 i + (l >> 5),
 //            piece ((((l & 31) >> 2) ^ (k-row & 7)) << 2) | (l & 3)
+// (i = 0 .. kDma-1).
 // No registers hold the staged data.
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -105,24 +110,24 @@ __device__ __forceinline__ void dma16(const void* g, u32x4* tile, int slot0) {
 }
 
 // K-mode row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_k_row(int i) { return 64 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3); }
-__device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 7) ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int dma_k_row(int i) { return 64 * (threadIdx.x >> 6) + 16 * i + ((threadIdx.x & 63) >> 2); }
+__device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 3) ^ ((row >> 2) & 3); }
 // MN-mode k-row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_mn_krow(int i) { return 16 * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
+__device__ __forceinline__ int dma_mn_krow(int i) { return 8 * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
 __device__ __forceinline__ int dma_mn_piece(int krow) {
   const int l = threadIdx.x & 31;
   return (((l >> 2) ^ (krow & 7)) << 2) | (l & 3);
 }
-__device__ __forceinline__ int dma_slot0(int i) { return 64 * (8 * (threadIdx.x >> 6) + i); }
+__device__ __forceinline__ int dma_slot0(int i) { return 64 * (kDma * (threadIdx.x >> 6) + i); }
 
-// K-mode loader over eight rows whose pointers (with the piece offset) are
+// K-mode loader over kDma rows whose pointers (with the piece offset) are
 // resolved once: pointer i is for row dma_k_row(i).
 struct RowsK8 {
-  const uint16_t* p[8];
+  const uint16_t* p[kDma];
   __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
     const int o = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(p[i] + o, tile, dma_slot0(i));
+    for (int i = 0; i < kDma; ++i) dma16(p[i] + o, tile, dma_slot0(i));
   }
 };
 
@@ -130,7 +135,7 @@ struct RowsK8 {
 __device__ __forceinline__ RowsK8 rows_k_strided(const uint16_t* base, int last, int ld) {
   RowsK8 R;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kDma; ++i) {
     const int row = dma_k_row(i);
     R.p[i] = base + (size_t)min(row, last) * ld + dma_k_seg(row) * 8;
   }
@@ -142,7 +147,7 @@ __device__ __forceinline__ RowsK8 rows_k_gather(const uint16_t* base, const int3
                                                int ld) {
   RowsK8 R;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kDma; ++i) {
     const int row = dma_k_row(i);
     R.p[i] = base + (size_t)idx[min(first + row, n_last)] * ld + dma_k_seg(row) * 8;
   }
@@ -180,57 +185,74 @@ __device__ __forceinline__ void mma16(const Frags& f, Acc& acc) {
 #undef RLK_MMA
 }
 
-// The four k steps of one 64-wide k-block from LDS stage `cur`; the
-// fragments of step kk+1 are read from LDS while the 16 MFMAs of step kk
-// run.  sched_barrier(0) pins this order (otherwise the scheduler sinks
-// each LDS read to its first use and every step waits on LDS).
 template <bool A_MN, bool B_MN>
-__device__ __forceinline__ void mma_block(const u32x4* __restrict__ cur, int wm, int wn, int lane, Acc& acc) {
-  const int ra0 = 128 * wm, rb0 = 128 * wn;
-  const u32x4* sA = cur;
-  const u32x4* sB = cur + kTileU4;
-  Frags f0, f1;
-  load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, 0, lane, f0);
-  load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, 1, lane, f1);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(f0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, 2, lane, f0);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(f1, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, 3, lane, f1);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(f0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16(f1, acc);
+__device__ __forceinline__ void load_block(const u32x4* __restrict__ stage, int wm, int wn, int lane, Frags& f0,
+                                           Frags& f1) {
+  const u32x4* sA = stage;
+  const u32x4* sB = stage + kTileU4;
+  load_frags<A_MN, B_MN>(sA, sB, 128 * wm, 128 * wn, 0, lane, f0);
+  load_frags<A_MN, B_MN>(sA, sB, 128 * wm, 128 * wn, 1, lane, f1);
 }
 
-// nk k-blocks of 64.  LA / LB: loaders with dma(kt, tile) that issue this
-// thread's direct global->LDS loads of k-block kt.  Two LDS stages: the
-// loads of block kt+1 are in flight while block kt is multiplied.
+// Wait until at most n of this thread's direct loads are outstanding (loads
+// complete in issue order, so everything older has landed in LDS).
+__device__ __forceinline__ void wait_dma(int n) {
+  if (n >= 2 * 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+static_assert(2 * kDma == 8, "wait_dma counts assume 8 loads per k-block");
+
+// nk k-blocks of kBK.  LA / LB: loaders with dma(kt, tile) that issue this
+// thread's direct global->LDS loads of k-block kt into a ring of kNS LDS
+// stages.  Per k-block (two MFMA k steps of 16 MFMAs each):
+//   MFMAs of step 0 | wait for block kt+1, barrier, issue the loads of
+//   block kt+3, read block kt+1's fragments | MFMAs of step 1
+// so the barrier sits between MFMA bursts and the next block's LDS reads
+// overlap the second burst.  The ring: stage of kt (its fragments are in
+// registers), kt+1 (read after the barrier), kt+2 (in flight), and kt+3
+// written into the stage of kt-1, which nobody reads any more.  Bare
+// s_barrier: __syncthreads() would add a release fence that waits for all
+// outstanding loads, including the later k-blocks still in flight.
 template <bool A_MN, bool B_MN, class LA, class LB>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wn = w >> 1;
-  u32x4* s0 = lds;
-  u32x4* s1 = lds + kStageU4;
-  la.dma(0, s0);
-  lb.dma(0, s0 + kTileU4);
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool odd = kt & 1;
-    const u32x4* cur = odd ? s1 : s0;
-    u32x4* nxt = odd ? s0 : s1;
-    // this thread's loads of block kt have landed; after the barrier every
-    // thread's have, and nobody reads `nxt` (block kt-1) any more
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) {
-      la.dma(kt + 1, nxt);
-      lb.dma(kt + 1, nxt + kTileU4);
+  static_assert(kNS == 4, "ring schedule written for four stages");
+#pragma unroll
+  for (int s = 0; s < kNS - 1; ++s)
+    if (s < nk) {
+      la.dma(s, lds + s * kStageU4);
+      lb.dma(s, lds + s * kStageU4 + kTileU4);
     }
-    mma_block<A_MN, B_MN>(cur, wm, wn, lane, acc);
+  wait_dma(2 * kDma * min(kNS - 2, nk - 1));
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  load_block<A_MN, B_MN>(lds, wm, wn, lane, f0, f1);
+  int nxt = 1;  // stage of block kt+1
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    Frags g0, g1;
+    if (kt + 1 < nk) {
+      wait_dma(2 * kDma * min(kNS - 3, nk - 2 - kt));
+      __builtin_amdgcn_s_barrier();
+      const int nb = kt + kNS - 1;
+      if (nb < nk) {
+        const int st = (nxt + kNS - 2) & (kNS - 1);  // stage of block kt-1
+        la.dma(nb, lds + st * kStageU4);
+        lb.dma(nb, lds + st * kStageU4 + kTileU4);
+      }
+      load_block<A_MN, B_MN>(lds + nxt * kStageU4, wm, wn, lane, g0, g1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(f1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    f0 = g0;
+    f1 = g1;
+    nxt = (nxt + 1) & (kNS - 1);
   }
   __syncthreads();
 }
@@ -254,6 +276,20 @@ __device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
 __device__ __forceinline__ int xcd_tile(int per) {
   const int bid = blockIdx.x;
   return (bid & 7) * per + (bid >> 3);
+}
+
+// Tile id -> (fast index f < F, slow index c < C) in groups of GM fast
+// indices: consecutive ids walk GM values of f, then the next c, so the
+// ~32 tiles in flight on one XCD form a GM x (32 / GM) block of the output
+// and share their operand rows in L2.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void grouped_tile(int id, int F, int& f, int& c, int C) {
+  const int per_group = kGroupM * C;
+  const int grp = id / per_group;
+  const int gm = min(kGroupM, F - grp * kGroupM);
+  const int within = id - grp * per_group;
+  c = within / gm;
+  f = grp * kGroupM + (within - c * gm);
 }
 
 }  // namespace rlk

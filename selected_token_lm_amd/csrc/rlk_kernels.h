@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.tg.per);
   if (id >= a.tg.row_tiles * a.nsplit * a.tg.tps) return;
-  const int ct = id / a.tg.row_tiles, rt = id - ct * a.tg.row_tiles;
+  int rt, ct;
+  grouped_tile(id, a.tg.row_tiles, rt, ct, a.nsplit * a.tg.tps);
   const int n_act = *a.n_act;
   const int i0 = rt * kBM;
   if (i0 >= n_act) return;
@@ -361,7 +362,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.tg.per);
   if (id >= a.tg.row_tiles * a.bg.G * a.tg.tps) return;
-  const int ct = id / a.tg.row_tiles, rt = id - ct * a.tg.row_tiles;
+  int rt, ct;
+  grouped_tile(id, a.tg.row_tiles, rt, ct, a.bg.G * a.tg.tps);
   const int n_act = *a.n_act;
   const int i0 = rt * kBM;
   if (i0 >= n_act) return;
@@ -423,11 +425,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // row 64 kt + t at this tile's columns (dz columns for grad_W's A operand,
 // compacted hidden rows for its B operand).
 struct ColsMN {
-  const uint16_t* col[8];  // matrix + column of piece i (row 0)
+  const uint16_t* col[kDma];  // matrix + column of piece i (row 0)
   int ld;
   __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(col[i] + (size_t)(kt * kBK + dma_mn_krow(i)) * ld, tile, dma_slot0(i));
+    for (int i = 0; i < kDma; ++i) dma16(col[i] + (size_t)(kt * kBK + dma_mn_krow(i)) * ld, tile, dma_slot0(i));
   }
 };
 
@@ -435,14 +437,14 @@ struct ColsMN {
 // group -> split sc = kg / S_pad, row (c_lo + sc) * S + kg % S_pad (clamped
 // to V - 1; those rows meet dz = 0).
 struct WRowsMN {
-  const uint16_t* col[8];  // W + column of piece i
+  const uint16_t* col[kDma];  // W + column of piece i
   int H, S, S_pad, c_lo, V;
   __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
     const int kg = kt * kBK;
     const int sc = kg / S_pad;
     const int base = (c_lo + sc) * S + (kg - sc * S_pad);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kDma; ++i)
       dma16(col[i] + (size_t)min(base + dma_mn_krow(i), V - 1) * H, tile, dma_slot0(i));
   }
 };
@@ -468,7 +470,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.per);
   if (id >= a.n_tiles * a.bg.G * a.tps) return;
-  const int vt = id / a.n_tiles, nt = id - vt * a.n_tiles;
+  int nt, vt;
+  grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps);
   const int sc = vt / a.tps, j = vt - sc * a.tps;
   const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   A.ld = a.bg.ldz;
   B.ld = a.H;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kDma; ++i) {
     const int p8 = dma_mn_piece(dma_mn_krow(i)) * 8;
     A.col[i] = a.dZ + (size_t)sc * a.bg.S_pad + min(v0 + p8, a.bg.S_pad - 8);
     B.col[i] = a.hA + min(n0 + p8, a.H - 8);
@@ -529,7 +532,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.per);
   if (id >= a.n_tiles * a.row_tiles) return;
-  const int rt = id / a.n_tiles, nt = id - rt * a.n_tiles;
+  int rt, nt;
+  grouped_tile(id, a.row_tiles, rt, nt, a.n_tiles);
   const int n_act = *a.n_act;
   const int i0 = rt * kBM, n0 = nt * kBN;
   if (i0 >= n_act) return;
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   B.c_lo = a.bg.c_lo;
   B.V = a.gm.V;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) B.col[i] = a.W + min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8);
+  for (int i = 0; i < kDma; ++i) B.col[i] = a.W + min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8);
   gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
