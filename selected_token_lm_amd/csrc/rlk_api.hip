@@ -59,7 +59,7 @@ Geom geom_of(int64_t V_global) {
 
 // --- workspace layouts -------------------------------------------------------
 struct FwdWs {
-  size_t idx, n_act, zt, rec, total;
+  size_t idx, yA, n_act, zt, rec, total;
   int64_t rec_chunks;
 };
 
@@ -68,6 +68,8 @@ FwdWs fwd_layout(int64_t T, int64_t V) {
   FwdWs w;
   size_t off = 0;
   w.idx = off;
+  off = align256(off + sizeof(int32_t) * T);
+  w.yA = off;
   off = align256(off + sizeof(int32_t) * T);
   w.n_act = off;
   off = align256(off + sizeof(int32_t));
@@ -94,7 +96,7 @@ int64_t dz_budget_bytes() {
 }
 
 struct BwdWs {
-  size_t idx, n_act, hA, dZ, ghacc, total;
+  size_t idx, n_act, rowinfo, hA, dZ, ghacc, total;
   int64_t T_pad, S_pad, G;
 };
 
@@ -112,6 +114,8 @@ BwdWs bwd_layout(int64_t T, int64_t H, int64_t V) {
   off = align256(off + sizeof(int32_t) * T);
   w.n_act = off;
   off = align256(off + sizeof(int32_t));
+  w.rowinfo = off;
+  off = align256(off + 16 * (size_t)w.T_pad);
   w.hA = off;
   off = align256(off + 2 * (size_t)w.T_pad * H);
   w.dZ = off;
@@ -206,6 +210,16 @@ struct ProfScope {
     RLK_TRY(launched(#kern));                                         \
   } while (0)
 
+// Same for a kernel given as a function pointer, timed under `name`.
+#define RLK_LAUNCH_FN(name, fn, grid, block, st, ...)           \
+  do {                                                          \
+    {                                                           \
+      ProfScope _ps(name, st);                                  \
+      hipLaunchKernelGGL(fn, grid, block, 0, st, __VA_ARGS__);  \
+    }                                                           \
+    RLK_TRY(launched(name));                                    \
+  } while (0)
+
 // Shapes first; with T == 0 there is nothing to read or write, so the
 // pointers are not checked (empty tensors may carry NULL).
 rlk_status check_common(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V) {
@@ -245,12 +259,13 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   const FwdWs L = fwd_layout(T, V_global);
   char* base = static_cast<char*>(ws);
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+  int32_t* yA = reinterpret_cast<int32_t*>(base + L.yA);
   int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
   float* zt = reinterpret_cast<float*>(base + L.zt);
   float2* rec = reinterpret_cast<float2*>(base + L.rec);
   rlk::PartialRec* pr = reinterpret_cast<rlk::PartialRec*>(pout);
 
-  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, n_act,
+  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, yA, n_act,
              mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
 
   rlk::SplitGeom gm;
@@ -262,7 +277,7 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   rlk::FwdArgs fa;
   fa.h = static_cast<const uint16_t*>(h);
   fa.W = static_cast<const uint16_t*>(W);
-  fa.y = y;
+  fa.yA = yA;
   fa.idx = idx;
   fa.n_act = n_act;
   fa.H = (int)H;
@@ -381,14 +396,16 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   char* base = static_cast<char*>(ws);
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
   int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
+  float4* rowinfo = reinterpret_cast<float4*>(base + L.rowinfo);
   uint16_t* dZ = reinterpret_cast<uint16_t*>(base + L.dZ);
   uint16_t* hA = reinterpret_cast<uint16_t*>(base + L.hA);
   float* ghacc = reinterpret_cast<float*>(base + L.ghacc);
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
 
-  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, n_act, nullptr, nullptr, nullptr);
-  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, hA);
+  RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, nullptr, n_act, nullptr, nullptr,
+             nullptr);
+  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, y, lse, g, hA, rowinfo);
   if (grad_h) {
     RLK_LAUNCH(zero_rows, dim3((unsigned)T), dim3(256), st, y, ignore_index, (int)H, static_cast<uint16_t*>(grad_h));
   }
@@ -416,11 +433,8 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
     rlk::DzArgs da;
     da.hA = hA;
     da.W = Wb;
-    da.y = y;
-    da.idx = idx;
+    da.rowinfo = rowinfo;
     da.n_act = n_act;
-    da.lse = lse;
-    da.g = g;
     da.H = (int)H;
     da.gm = gm;
     da.tg.tps = tps;
@@ -457,11 +471,12 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
       ha.n_tiles = n_tiles;
       ha.row_tiles = row_tiles;
       ha.per = (int)ceil_div((int64_t)n_tiles * row_tiles, 8);
-      ha.first = c_lo == 0;
-      ha.last = c_lo + G > last_split;
       ha.ghacc = ghacc;
       ha.grad_h = static_cast<uint16_t*>(grad_h);
-      RLK_LAUNCH(gradh_tiles, dim3((unsigned)(8 * ha.per)), dim3(rlk::kThreads), st, ha);
+      const bool first = c_lo == 0, last = c_lo + G > last_split;
+      void (*kfn)(rlk::GradHArgs) = first ? (last ? rlk::gradh_tiles<true, true> : rlk::gradh_tiles<true, false>)
+                                          : (last ? rlk::gradh_tiles<false, true> : rlk::gradh_tiles<false, false>);
+      RLK_LAUNCH_FN("gradh_tiles", kfn, dim3((unsigned)(8 * ha.per)), dim3(rlk::kThreads), st, ha);
     }
   }
   return ok();

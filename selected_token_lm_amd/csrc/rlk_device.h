@@ -62,11 +62,20 @@ __device__ __forceinline__ MS ms_pairwise_tree(MS* v, int n) {
   return v[0];
 }
 
-// Round fp32 to bf16, round-to-nearest-even (inputs are finite).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 values rounded to bf16 (round to nearest even, v_cvt_pk_bf16_f32),
+// packed with `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Lane pair (l, l ^ 32): the value of lane l & 31 (lo) and of lane
+// (l & 31) + 32 (hi), in both lanes (v_permlane32_swap).
+__device__ __forceinline__ void lane_halves(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
 }
 
 }  // namespace rlk

@@ -11,11 +11,16 @@
 // (256 accumulator registers).  A 128-column vocabulary chunk of a row
 // therefore lives inside one wave.
 //
-// MFMA register layouts (32x32x16 bf16):
-//   A operand, lane l: row (l & 31), k = 8*(l >> 5) + 0..7 of the k step
-//   B operand, lane l: col (l & 31), same k
-//   D, lane l, element r (0..15): row 8*(r>>2) + 4*(l>>5) + (r&3), col l & 31
-// A and B use the same k assignment, so a step sums exactly its 16 k values.
+// MFMA register layouts (32x32x16 bf16, D = X * Y^T):
+//   X operand, lane l: row (l & 31), k = 8*(l >> 5) + 0..7 of the k step
+//   Y operand, lane l: row (l & 31), same k
+//   D, lane l, element r (0..15): X-row 8*(r>>2) + 4*(l>>5) + (r&3), Y-row l & 31
+// X and Y use the same k assignment, so a step sums exactly its 16 k values.
+// The tile's B fragments go in as X and its A fragments as Y, so that lane l
+// of block (mi, ni) holds tile row 32 mi + (l & 31) and, in elements
+// 4g .. 4g+3, the four consecutive tile columns 32 ni + 8 g + 4 (l >> 5) + 0..3:
+// a row's values sit in one lane pair (l, l ^ 32) and stores write 4
+// consecutive columns per lane.
 //
 // Operands come in one of two global layouts:
 //   K mode : rows of the operand are contiguous in k (h [T,H], W [V,H], dz
@@ -31,8 +36,11 @@
 // Both LDS layouts are XOR-swizzled so that the 16 lanes served per LDS
 // cycle hit distinct banks.
 //
-// Pipelined: k-blocks of 32 are loaded straight from global memory into a
-// ring of four LDS stages, three k-blocks ahead of the MFMAs.
+// Pipelined: k-blocks of 64 are loaded straight from global memory into two
+// LDS stages, one k-block ahead of the MFMAs.  A K-mode row contributes 128
+// contiguous bytes per k-block (one full cache line), which halves the
+// number of memory requests per byte compared with 32-wide k-blocks: the
+// direct loads are limited by the requests a CU can keep in flight.
 #pragma once
 
 #include "rlk_device.h"
@@ -44,20 +52,22 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // registers in private memory)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
 constexpr int kMI = 4, kNI = 4;            // 32 x 32 blocks per wave
 constexpr int kKK = kBK / 16;              // MFMA k steps per k-block
 constexpr int kSegs = kBK / 8;             // 16-byte pieces per K-mode row
 constexpr int kDma = kBK / 8;              // direct-load instructions per wave per operand per k-block
-constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (16 KB)
-constexpr int kStageU4 = 2 * kTileU4;      // A + B
-constexpr int kNS = 4;                     // LDS stages (k-blocks in the ring)
+constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (32 KB)
+constexpr int kTileU4Check = 256 * kBK / 8;
+static_assert(kTileU4 == kTileU4Check, "tile = 256 rows x kBK bf16");
+constexpr int kStageU4 = 2 * kTileU4;      // A + B (64 KB)
+constexpr int kNS = 2;                     // LDS stages
 constexpr int kLdsU4 = kNS * kStageU4;     // 128 KB
 
-// K-mode slot of (row, 16-byte piece seg), 64-byte rows: four consecutive
+// K-mode slot of (row, 16-byte piece seg), 128-byte rows: two consecutive
 // rows fill a 256-byte bank row and the piece index is xor-ed with
-// (row >> 2) & 3, so 16 consecutive rows of one k piece cover all banks.
-__device__ __forceinline__ int slot_k(int row, int seg) { return row * kSegs + (seg ^ ((row >> 2) & 3)); }
+// (row >> 1) & 7, so 16 consecutive rows of one k piece cover all banks.
+__device__ __forceinline__ int slot_k(int row, int seg) { return row * kSegs + (seg ^ ((row >> 1) & 7)); }
 
 // MN-mode slot of (k-row, 16-byte piece p of 32): 64-byte blocks of the row
 // xor-ed with (k-row & 7).
@@ -98,8 +108,8 @@ __device__ __forceinline__ bf16x8 frag_a(const u32x4* t, int r0, int kk, int lan
 // lane l at byte 16 l.  Instruction i of wave w covers tile slots
 // 64 (kDma w + i) .. +64, so lane l of it fills slot s = 64 (kDma w + i) + l and
 // fetches the global piece that the swizzled layout puts there:
-//   K mode : row 64 w + 16 i + (l >> 2), piece (l & 3) ^ ((row >> 2) & 3)
-//   MN mode: k-row 8 w + 2 i + (l >> 5),
+//   K mode : row 64 w + 8 i + (l >> 3), piece (l & 7) ^ ((row >> 1) & 7)
+//   MN mode: k-row 16 w + 2 i + (l >> 5),
 //            piece ((((l & 31) >> 2) ^ (k-row & 7)) << 2) | (l & 3)
 // (i = 0 .. kDma-1).
 // No registers hold the staged data.
@@ -110,10 +120,10 @@ __device__ __forceinline__ void dma16(const void* g, u32x4* tile, int slot0) {
 }
 
 // K-mode row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_k_row(int i) { return 64 * (threadIdx.x >> 6) + 16 * i + ((threadIdx.x & 63) >> 2); }
-__device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 3) ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int dma_k_row(int i) { return 64 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 7) ^ ((row >> 1) & 7); }
 // MN-mode k-row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_mn_krow(int i) { return 8 * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
+__device__ __forceinline__ int dma_mn_krow(int i) { return 16 * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
 __device__ __forceinline__ int dma_mn_piece(int krow) {
   const int l = threadIdx.x & 31;
   return (((l >> 2) ^ (krow & 7)) << 2) | (l & 3);
@@ -177,7 +187,7 @@ __device__ __forceinline__ void load_frags(const u32x4* __restrict__ sA, const u
 }
 
 __device__ __forceinline__ void mma16(const Frags& f, Acc& acc) {
-#define RLK_MMA(mi, ni, A, B) acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.A, f.B, acc.c[mi][ni], 0, 0, 0);
+#define RLK_MMA(mi, ni, A, B) acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.B, f.A, acc.c[mi][ni], 0, 0, 0);
   RLK_MMA(0, 0, a0, b0) RLK_MMA(0, 1, a0, b1) RLK_MMA(0, 2, a0, b2) RLK_MMA(0, 3, a0, b3)
   RLK_MMA(1, 0, a1, b0) RLK_MMA(1, 1, a1, b1) RLK_MMA(1, 2, a1, b2) RLK_MMA(1, 3, a1, b3)
   RLK_MMA(2, 0, a2, b0) RLK_MMA(2, 1, a2, b1) RLK_MMA(2, 2, a2, b2) RLK_MMA(2, 3, a2, b3)
@@ -185,74 +195,71 @@ __device__ __forceinline__ void mma16(const Frags& f, Acc& acc) {
 #undef RLK_MMA
 }
 
-template <bool A_MN, bool B_MN>
-__device__ __forceinline__ void load_block(const u32x4* __restrict__ stage, int wm, int wn, int lane, Frags& f0,
-                                           Frags& f1) {
-  const u32x4* sA = stage;
-  const u32x4* sB = stage + kTileU4;
-  load_frags<A_MN, B_MN>(sA, sB, 128 * wm, 128 * wn, 0, lane, f0);
-  load_frags<A_MN, B_MN>(sA, sB, 128 * wm, 128 * wn, 1, lane, f1);
-}
-
-// Wait until at most n of this thread's direct loads are outstanding (loads
-// complete in issue order, so everything older has landed in LDS).
-__device__ __forceinline__ void wait_dma(int n) {
-  if (n >= 2 * 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+// Wait until at most n of this thread's vector memory operations are
+// outstanding (they complete in issue order, so everything older has landed).
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-static_assert(2 * kDma == 8, "wait_dma counts assume 8 loads per k-block");
+static_assert(2 * kDma == 16, "wait_vm counts assume 16 direct loads per k-block");
 
 // nk k-blocks of kBK.  LA / LB: loaders with dma(kt, tile) that issue this
-// thread's direct global->LDS loads of k-block kt into a ring of kNS LDS
-// stages.  Per k-block (two MFMA k steps of 16 MFMAs each):
-//   MFMAs of step 0 | wait for block kt+1, barrier, issue the loads of
-//   block kt+3, read block kt+1's fragments | MFMAs of step 1
-// so the barrier sits between MFMA bursts and the next block's LDS reads
-// overlap the second burst.  The ring: stage of kt (its fragments are in
-// registers), kt+1 (read after the barrier), kt+2 (in flight), and kt+3
-// written into the stage of kt-1, which nobody reads any more.  Bare
-// s_barrier: __syncthreads() would add a release fence that waits for all
-// outstanding loads, including the later k-blocks still in flight.
+// thread's direct global->LDS loads of k-block kt.  Two LDS stages: block kt
+// is read from stage kt & 1 while block kt+1 lands in the other one.  Per
+// k-block (four MFMA k steps of 16 MFMAs each):
+//   read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
+//   MFMAs step 2 | wait for block kt+1 and for this wave's reads, barrier,
+//   issue the loads of block kt+2 into stage kt & 1, read step 0 of block
+//   kt+1 | MFMAs step 3
+// so the one barrier per block sits between MFMA bursts, every LDS read
+// overlaps an MFMA burst, and after the barrier no wave reads stage kt & 1
+// any more.  Bare s_barrier: __syncthreads() would add a release fence that
+// waits for all outstanding loads, including the next block in flight.
 template <bool A_MN, bool B_MN, class LA, class LB>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  static_assert(kNS == 4, "ring schedule written for four stages");
-#pragma unroll
-  for (int s = 0; s < kNS - 1; ++s)
-    if (s < nk) {
-      la.dma(s, lds + s * kStageU4);
-      lb.dma(s, lds + s * kStageU4 + kTileU4);
-    }
-  wait_dma(2 * kDma * min(kNS - 2, nk - 1));
+  const int ra0 = 128 * (w & 1), rb0 = 128 * (w >> 1);
+  static_assert(kNS == 2 && kKK == 4, "schedule written for two stages of four k steps");
+  la.dma(0, lds);
+  lb.dma(0, lds + kTileU4);
+  if (nk > 1) {
+    la.dma(1, lds + kStageU4);
+    lb.dma(1, lds + kStageU4 + kTileU4);
+  }
+  wait_vm(nk > 1 ? 2 * kDma : 0);
   __builtin_amdgcn_s_barrier();
-  Frags f0, f1;
-  load_block<A_MN, B_MN>(lds, wm, wn, lane, f0, f1);
-  int nxt = 1;  // stage of block kt+1
+  Frags f;
+  load_frags<A_MN, B_MN>(lds, lds + kTileU4, ra0, rb0, 0, lane, f);
   for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(f0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    Frags g0, g1;
+    const u32x4* sA = lds + (kt & 1) * kStageU4;
+    const u32x4* sB = sA + kTileU4;
+    Frags g;
+#pragma unroll
+    for (int kk = 1; kk < kKK; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, kk, lane, g);
+      __builtin_amdgcn_sched_barrier(0);
+      mma16(f, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      f = g;
+    }
     if (kt + 1 < nk) {
-      wait_dma(2 * kDma * min(kNS - 3, nk - 2 - kt));
+      wait_vm(0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
-      const int nb = kt + kNS - 1;
-      if (nb < nk) {
-        const int st = (nxt + kNS - 2) & (kNS - 1);  // stage of block kt-1
-        la.dma(nb, lds + st * kStageU4);
-        lb.dma(nb, lds + st * kStageU4 + kTileU4);
+      if (kt + 2 < nk) {
+        u32x4* st = lds + (kt & 1) * kStageU4;
+        la.dma(kt + 2, st);
+        lb.dma(kt + 2, st + kTileU4);
       }
-      load_block<A_MN, B_MN>(lds + nxt * kStageU4, wm, wn, lane, g0, g1);
+      const u32x4* nA = lds + ((kt + 1) & 1) * kStageU4;
+      load_frags<A_MN, B_MN>(nA, nA + kTileU4, ra0, rb0, 0, lane, g);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mma16(f1, acc);
+    mma16(f, acc);
     __builtin_amdgcn_sched_barrier(0);
-    f0 = g0;
-    f1 = g1;
-    nxt = (nxt + 1) & (kNS - 1);
+    f = g;
   }
   __syncthreads();
 }
@@ -264,9 +271,13 @@ __device__ __forceinline__ void acc_zero(Acc& acc) {
     for (int ni = 0; ni < kNI; ++ni) acc.c[mi][ni] = f32x16{};
 }
 
-// Tile-local row of accumulator element r of block mi for lane l in wave (wm, *).
-__device__ __forceinline__ int acc_row(int wm, int mi, int r, int lane) {
-  return 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+// Tile-local row held by lane l in block mi of wave (wm, *).
+__device__ __forceinline__ int acc_row(int wm, int mi, int lane) { return 128 * wm + 32 * mi + (lane & 31); }
+
+// Tile-local column of elements 4g .. 4g+3 (first of four) of block ni for
+// lane l in wave (*, wn).
+__device__ __forceinline__ int acc_col4(int wn, int ni, int g, int lane) {
+  return 128 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own

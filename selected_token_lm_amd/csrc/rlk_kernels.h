@@ -18,7 +18,8 @@ namespace rlk {
 
 // ---------------------------------------------------------------------------
 // Active-row compaction.  One block of 1024 threads scans y in order, so the
-// list is the active rows in ascending order and independent of timing.
+// list is the active rows in ascending order and independent of timing;
+// yA (optional) receives their targets in the same order.
 // Inactive rows get their final outputs here: logp = lse = 0 (forward) or
 // the empty statistics {-inf, 0, 0, 0} (range partial).
 // ---------------------------------------------------------------------------
@@ -28,7 +29,8 @@ struct PartialRec {
 };
 
 __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__ y, int T, int ignore_index,
-                                                     int32_t* __restrict__ idx, int32_t* __restrict__ n_act,
+                                                     int32_t* __restrict__ idx, int32_t* __restrict__ yA,
+                                                     int32_t* __restrict__ n_act,
                                                      float* __restrict__ logp, float* __restrict__ lse,
                                                      PartialRec* __restrict__ pout) {
   __shared__ int wave_tot[16];
@@ -38,7 +40,8 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
   __syncthreads();
   for (int t0 = 0; t0 < T; t0 += 1024) {
     const int t = t0 + tid;
-    const bool act = (t < T) && (y[t] != ignore_index);
+    const int yt = (t < T) ? y[t] : ignore_index;
+    const bool act = yt != ignore_index;
     if (t < T && !act) {
       if (logp) logp[t] = 0.f;
       if (lse) lse[t] = 0.f;
@@ -50,7 +53,10 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
     __syncthreads();
     int off = base_s;
     for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (act) idx[off + before] = t;
+    if (act) {
+      idx[off + before] = t;
+      if (yA) yA[off + before] = yt;
+    }
     __syncthreads();
     if (tid == 0) {
       int tot = 0;
@@ -81,8 +87,32 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
   c1 = min(c0 + kChunk, send);
 }
 
-__device__ __forceinline__ float xor_max(float v, int d) { return fmaxf(v, __shfl_xor(v, d, 64)); }
-__device__ __forceinline__ float xor_add(float v, int d) { return v + __shfl_xor(v, d, 64); }
+// Element k = 16 ni + r (ni = 0..3, r = 0..15) of one row block of the
+// accumulator, selected by a per-lane k (a chain of compares and selects;
+// indexing a register array with k would move the array to memory).
+__device__ __forceinline__ float pick64(const f32x16 (&c)[kNI], int k) {
+  float v = 0.f;
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v = (k == 16 * ni + r) ? c[ni][r] : v;
+  return v;
+}
+
+// Balanced pairwise tree over e[0..63]: adjacent pairs, then pairs of pairs.
+// (Fixed-size levels: every index is a compile-time constant.)
+__device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
+  float t32[32], t16[16], t8[8], t4[4];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) t32[k] = e[2 * k] + e[2 * k + 1];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t16[k] = t32[2 * k] + t32[2 * k + 1];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) t8[k] = t16[2 * k] + t16[2 * k + 1];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) t4[k] = t8[2 * k] + t8[2 * k + 1];
+  return (t4[0] + t4[1]) + (t4[2] + t4[3]);
+}
 
 // ---------------------------------------------------------------------------
 // Forward chunk statistics on 256 x 256 tiles.
@@ -93,13 +123,14 @@ __device__ __forceinline__ float xor_add(float v, int d) { return v + __shfl_xor
 // (g = local split * cps + chunk) for active row i, and zt[i] = the target's
 // logit, written by the one chunk that holds it.
 //
-// Chunk statistics of one row over the chunk's valid columns
-// c = 32 b + q (b = 0..3 MFMA column block, q = 0..31 lane):
-//   m = max_c z_c (exact);
-//   e_c = exp(z_c - m), 0 for invalid columns;
-//   a_q = ((e_q + e_{32+q}) + e_{64+q}) + e_{96+q};
-//   s = pairwise tree over q = 0..31 of a_q (xor butterfly; every lane ends
-//       with the same value because fp addition is commutative).
+// A row's 128 chunk columns sit in one lane pair: the lane of half h
+// (h = 0, 1) holds the 64 columns c with (c >> 2) & 1 == h, in ascending
+// order as its elements k = 16 ni + r (column 32 ni + 8 (r >> 2) + 4 h + (r & 3)).
+// Chunk statistics of one row over the chunk's valid columns:
+//   m   = max_c z_c (exact; invalid columns enter as -inf);
+//   e_c = exp(z_c - m) (0 for invalid columns);
+//   s   = T(e of half 0) + T(e of half 1), T = balanced pairwise tree over
+//         the half's 64 columns in ascending order.
 // ---------------------------------------------------------------------------
 struct TileGeom {
   int tps;        // 256-column tiles per split = ceil(S / 256)
@@ -110,7 +141,7 @@ struct TileGeom {
 struct FwdArgs {
   const uint16_t* h;
   const uint16_t* W;
-  const int32_t* y;
+  const int32_t* yA;  // targets of the active rows, compacted
   const int32_t* idx;
   const int32_t* n_act;
   int H;
@@ -138,78 +169,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (c0 >= send) return;
   const int c1 = min(c0 + kBN, send);
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, hh = lane >> 5;
+  // targets of this lane's rows, loaded ahead of the main loop
+  int tgt[kMI];
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi) tgt[mi] = a.yA[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
+
   const RowsK8 A = rows_k_gather(a.h, a.idx, i0, n_act - 1, a.H);
   const RowsK8 B = rows_k_strided(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
   Acc acc;
   acc_zero(acc);
   gemm256<false, false>(A, B, a.H / kBK, acc, lds);
 
-  // targets of the tile's rows, staged in LDS (the main loop ended with a barrier)
-  int* ys = reinterpret_cast<int*>(lds);
-  if (tid < kBM) {
-    const int i = i0 + tid;
-    ys[tid] = (i < n_act) ? a.y[a.idx[i]] : -1;
-  }
-  __syncthreads();
-
-  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
   const int cc0 = c0 + kChunk * wn;  // this wave's chunk
   const int width = min(cc0 + kChunk, c1) - cc0;
   if (width <= 0) return;
   const int g = sl * a.gm.cps + 2 * j + wn;
-  bool valid[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) valid[b] = (32 * b + q) < width;
+  const int lim = width - 4 * hh;  // element (ni, r) is valid iff 32 ni + 8 (r >> 2) + (r & 3) < lim
 
-  float keep_m[kMI] = {}, keep_s[kMI] = {};
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
+    const int i = i0 + acc_row(wm, mi, lane);
+    const int tc = tgt[mi] - cc0;
+    if (i < n_act && tc >= 0 && tc < width && ((tc >> 2) & 1) == hh)
+      a.zt[i] = pick64(acc.c[mi], ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3));
+    if (width < kChunk) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float mx = -INFINITY;
+      for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (valid[b]) mx = fmaxf(mx, acc.c[mi][b][rr]);
-      mx = xor_max(mx, 1);
-      mx = xor_max(mx, 2);
-      mx = xor_max(mx, 4);
-      mx = xor_max(mx, 8);
-      mx = xor_max(mx, 16);
-      float e[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) e[b] = valid[b] ? rlk_exp(acc.c[mi][b][rr] - mx) : 0.f;
-      float s = ((e[0] + e[1]) + e[2]) + e[3];
-      s = xor_add(s, 1);
-      s = xor_add(s, 2);
-      s = xor_add(s, 4);
-      s = xor_add(s, 8);
-      s = xor_add(s, 16);
-      if (q == rr) {
-        keep_m[mi] = mx;
-        keep_s[mi] = s;
-      }
-      const int row = acc_row(wm, mi, rr, lane);
-      const int tc = ys[row] - cc0;
-      if (tc >= 0 && tc < width && (tc & 31) == q) {
-        const int b = tc >> 5;
-        float v = acc.c[mi][0][rr];
-        v = (b == 1) ? acc.c[mi][1][rr] : v;
-        v = (b == 2) ? acc.c[mi][2][rr] : v;
-        v = (b == 3) ? acc.c[mi][3][rr] : v;
-        a.zt[i0 + row] = v;
-      }
+        for (int r = 0; r < 16; ++r)
+          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) acc.c[mi][ni][r] = -INFINITY;
     }
-  }
-  if (q < 16) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      const int i = i0 + acc_row(wm, mi, q, lane);
-      if (i < n_act) a.rec[(size_t)g * a.rec_stride + i] = make_float2(keep_m[mi], keep_s[mi]);
-    }
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc.c[mi][ni][r]);
+    float lo, hi;
+    lane_halves(mx, lo, hi);
+    mx = fmaxf(lo, hi);
+    float e[64];
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[16 * ni + r] = rlk_exp(acc.c[mi][ni][r] - mx);
+    lane_halves(tree_sum64(e), lo, hi);
+    if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = make_float2(mx, lo + hi);
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Split fold + tree + epilogue.  grid.x: 64 active rows per block; 8 waves,
@@ -340,13 +347,10 @@ struct BwdGeom {
 };
 
 struct DzArgs {
-  const uint16_t* hA;  // active rows of h, compacted, zero padded to T_pad
+  const uint16_t* hA;       // active rows of h, compacted, zero padded to T_pad
   const uint16_t* W;
-  const int32_t* y;
-  const int32_t* idx;
+  const float4* rowinfo;    // per active row {lse, g, target (bits), 0}; {0, 0, -1, 0} past n_act
   const int32_t* n_act;
-  const float* lse;
-  const float* g;
   int H;
   SplitGeom gm;
   TileGeom tg;
@@ -357,7 +361,7 @@ struct DzArgs {
 // dz for the group's splits on 256 x 256 tiles (same tiles and logits as the
 // forward): p = exp(z - lse_i), dz = g_i * ([v == y_i] - p) in fp32, rounded
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
-// are written as zeros.
+// are written as zeros.  Each lane stores four consecutive columns (8 bytes).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dz_tiles(DzArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.tg.per);
@@ -372,7 +376,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));  // columns of this split
   const int c0 = sbeg + j * kBN;
   const int c1 = sbeg + min(j * kBN + kBN, valid_s);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  float4 ri[kMI];  // this lane's rows, loaded ahead of the main loop
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, lane)];
   Acc acc;
   acc_zero(acc);
   if (c0 < c1) {
@@ -380,43 +387,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const RowsK8 B = rows_k_strided(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
     gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
-  float* rv = reinterpret_cast<float*>(lds);  // [256] lse, [256] g, [256] y
-  int* ry = reinterpret_cast<int*>(lds) + 2 * kBM;
-  if (tid < kBM) {
-    const int i = i0 + tid;
-    if (i < n_act) {
-      const int t = a.idx[i];
-      rv[tid] = a.lse[t];
-      rv[kBM + tid] = a.g[t];
-      ry[tid] = a.y[t];
-    } else {
-      rv[tid] = 0.f;
-      rv[kBM + tid] = 0.f;
-      ry[tid] = -1;
-    }
-  }
-  __syncthreads();
-  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int vl = j * kBN + kChunk * wn + 32 * b + q;  // column within the split
-    if (vl >= a.bg.S_pad) continue;
-    const bool cvalid = vl < valid_s;
-    const int v = sbeg + vl;
+  for (int mi = 0; mi < kMI; ++mi) {
+    const int i = i0 + acc_row(wm, mi, lane);
+    const bool rvalid = i < n_act;
+    const float L = ri[mi].x, gi = ri[mi].y;
+    const int yl = __float_as_int(ri[mi].z) - sbeg;  // target column within the split
+    uint16_t* drow = dzs + (size_t)i * a.bg.ldz;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = acc_row(wm, mi, rr, lane);
-        const int i = i0 + row;
-        float d = 0.f;
-        if (cvalid && i < n_act) {
-          const float p = rlk_exp(acc.c[mi][b][rr] - rv[row]);
-          const float delta = (ry[row] == v) ? 1.f : 0.f;
-          d = rv[kBM + row] * (delta - p);
+      for (int q = 0; q < 4; ++q) {
+        if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform
+        const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int vl = vl0 + e;
+          const float p = rlk_exp(acc.c[mi][ni][4 * q + e] - L);
+          const float delta = (vl == yl) ? 1.f : 0.f;
+          d[e] = (rvalid && vl < valid_s) ? gi * (delta - p) : 0.f;
         }
-        dzs[(size_t)i * a.bg.ldz + vl] = f32_to_bf16_rne(d);
+        *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
       }
   }
 }
@@ -492,18 +485,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   Acc acc;
   acc_zero(acc);
   gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
-  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
   float* out = a.grad_W + (size_t)sbeg * a.H;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = n0 + 128 * wn + 32 * ni + q;
-    if (n >= a.H) continue;
+  for (int mi = 0; mi < kMI; ++mi) {
+    const int v = v0 + acc_row(wm, mi, lane);
+    if (v >= valid_s) continue;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int v = v0 + acc_row(wm, mi, rr, lane);
-        if (v < valid_s) out[(size_t)v * a.H + n] = acc.c[mi][ni][rr];
+      for (int q = 0; q < 4; ++q) {
+        if (n0 + 128 * wn + 32 * ni + 8 * q >= a.H) continue;  // wave-uniform
+        const f32x16& c = acc.c[mi][ni];
+        *reinterpret_cast<float4*>(out + (size_t)v * a.H + n0 + acc_col4(wn, ni, q, lane)) =
+            make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
       }
   }
 }
@@ -519,7 +514,6 @@ struct GradHArgs {
   int n_tiles;    // 256-column tiles of H
   int row_tiles;  // 256-row tiles covering T
   int per;
-  int first, last;
   float* ghacc;
   uint16_t* grad_h;
 };
@@ -528,6 +522,9 @@ struct GradHArgs {
 // group's padded columns.  A (dz rows) is K mode, B (W rows) MN mode.  The
 // fp32 chain continues across groups through ghacc (exact store/load); after
 // the last group it is rounded to bf16 once and written to the row's place.
+// kFirst / kLast: the group is the first / last one (compile-time, so that
+// the accumulators never merge across a branch).
+template <bool kFirst, bool kLast>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gradh_tiles(GradHArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.per);
@@ -537,25 +534,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int n_act = *a.n_act;
   const int i0 = rt * kBM, n0 = nt * kBN;
   if (i0 >= n_act) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, q = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  int dst[kMI];  // output rows of this lane's active rows, loaded ahead
+  if (kLast) {
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) dst[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
+  }
   Acc acc;
   acc_zero(acc);
-  if (!a.first) {
+  if (!kFirst) {
     // continue the chain from the previous groups (rows/columns outside
     // the problem read a clamped, valid address; they are never stored)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int n = min(n0 + 128 * wn + 32 * ni + q, a.H - 1);
+    for (int mi = 0; mi < kMI; ++mi) {
+      const float* src = a.ghacc + (size_t)min(i0 + acc_row(wm, mi, lane), n_act - 1) * a.H;
 #pragma unroll
-      for (int mi = 0; mi < kMI; ++mi) {
+      for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int i = min(i0 + acc_row(wm, mi, rr, lane), n_act - 1);
-          acc.c[mi][ni][rr] = a.ghacc[(size_t)i * a.H + n];
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(src + min(n0 + acc_col4(wn, ni, q, lane), a.H - 4));
+          acc.c[mi][ni][4 * q] = v.x;
+          acc.c[mi][ni][4 * q + 1] = v.y;
+          acc.c[mi][ni][4 * q + 2] = v.z;
+          acc.c[mi][ni][4 * q + 3] = v.w;
         }
-        // bound the loads in flight (each block lands in its accumulator)
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // bound the loads in flight (each block lands in its accumulator)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   const RowsK8 A = rows_k_strided(a.dZ + (size_t)i0 * a.bg.ldz, kBM - 1, a.bg.ldz);
@@ -569,37 +573,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int i = 0; i < kDma; ++i) B.col[i] = a.W + min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8);
   gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int n = n0 + 128 * wn + 32 * ni + q;
-    if (n >= a.H) continue;
+  for (int mi = 0; mi < kMI; ++mi) {
+    const int i = i0 + acc_row(wm, mi, lane);
+    if (i >= n_act) continue;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int i = i0 + acc_row(wm, mi, rr, lane);
-        if (i >= n_act) continue;
-        if (a.last)
-          a.grad_h[(size_t)a.idx[i] * a.H + n] = f32_to_bf16_rne(acc.c[mi][ni][rr]);
+      for (int q = 0; q < 4; ++q) {
+        if (n0 + 128 * wn + 32 * ni + 8 * q >= a.H) continue;  // wave-uniform
+        const int n = n0 + acc_col4(wn, ni, q, lane);
+        const f32x16& c = acc.c[mi][ni];
+        if (kLast)
+          *reinterpret_cast<uint2*>(a.grad_h + (size_t)dst[mi] * a.H + n) =
+              make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
         else
-          a.ghacc[(size_t)i * a.H + n] = acc.c[mi][ni][rr];
+          *reinterpret_cast<float4*>(a.ghacc + (size_t)i * a.H + n) =
+              make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
       }
   }
 }
 
 
 // hA[i] = h[idx[i]] for active rows i < n_act, zero rows for n_act <= i <
-// rows.  grid rows, block 256; 16-byte pieces.
+// rows; rowinfo[i] = {lse, g, target, 0} of the row ({0, 0, -1, 0} past
+// n_act).  grid rows, block 256; 16-byte pieces.
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ n_act_p, int H,
-                                                   uint16_t* __restrict__ hA) {
+                                                   const int32_t* __restrict__ y, const float* __restrict__ lse,
+                                                   const float* __restrict__ g, uint16_t* __restrict__ hA,
+                                                   float4* __restrict__ rowinfo) {
   const int i = blockIdx.x;
   const int n_act = *n_act_p;
   u32x4* dst = reinterpret_cast<u32x4*>(hA + (size_t)i * H);
   if (i < n_act) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)idx[i] * H);
+    const int t = idx[i];
+    const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)t * H);
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
+    if (threadIdx.x == 0) rowinfo[i] = make_float4(lse[t], g[t], __int_as_float(y[t]), 0.f);
   } else {
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
   }
 }
 
