@@ -59,13 +59,14 @@ Geom geom_of(int64_t V_global) {
 
 // --- workspace layouts -------------------------------------------------------
 struct FwdWs {
-  size_t idx, yA, n_act, zt, rec, total;
-  int64_t rec_chunks;
+  size_t idx, yA, n_act, zt, hA, rec, total;
+  int64_t rec_chunks, T_pad;
 };
 
 // Record slots: one per (chunk of the full vocabulary of V rows, row).
-FwdWs fwd_layout(int64_t T, int64_t V) {
+FwdWs fwd_layout(int64_t T, int64_t H, int64_t V) {
   FwdWs w;
+  w.T_pad = ceil_div(std::max<int64_t>(T, 1), rlk::kBM) * rlk::kBM;
   size_t off = 0;
   w.idx = off;
   off = align256(off + sizeof(int32_t) * T);
@@ -75,6 +76,8 @@ FwdWs fwd_layout(int64_t T, int64_t V) {
   off = align256(off + sizeof(int32_t));
   w.zt = off;
   off = align256(off + sizeof(float) * T);
+  w.hA = off;
+  off = align256(off + 2 * (size_t)w.T_pad * H);
   w.rec_chunks = rlk::kNSplit * geom_of(V).cps;
   w.rec = off;
   off = align256(off + sizeof(float2) * (size_t)w.rec_chunks * (size_t)T);
@@ -256,17 +259,20 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
                        int32_t ignore_index, int s0, int nsplit, int64_t vocab_start, int64_t vocab_len, int mode,
                        float* logp, float* lse, rlk_lse_partial_t* pout, void* ws, hipStream_t st) {
   const Geom g = geom_of(V_global);
-  const FwdWs L = fwd_layout(T, V_global);
+  const FwdWs L = fwd_layout(T, H, V_global);
   char* base = static_cast<char*>(ws);
   int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
   int32_t* yA = reinterpret_cast<int32_t*>(base + L.yA);
   int32_t* n_act = reinterpret_cast<int32_t*>(base + L.n_act);
   float* zt = reinterpret_cast<float*>(base + L.zt);
+  uint16_t* hA = reinterpret_cast<uint16_t*>(base + L.hA);
   float2* rec = reinterpret_cast<float2*>(base + L.rec);
   rlk::PartialRec* pr = reinterpret_cast<rlk::PartialRec*>(pout);
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, yA, n_act,
              mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
+  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, static_cast<const uint16_t*>(h), idx, n_act,
+             (int)H, y, nullptr, nullptr, hA, nullptr);
 
   rlk::SplitGeom gm;
   gm.V = (int)g.V;
@@ -275,7 +281,7 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   gm.s0 = s0;
   gm.vocab_start = (int)vocab_start;
   rlk::FwdArgs fa;
-  fa.h = static_cast<const uint16_t*>(h);
+  fa.hA = hA;
   fa.W = static_cast<const uint16_t*>(W);
   fa.yA = yA;
   fa.idx = idx;
@@ -324,7 +330,7 @@ size_t rlk_workspace_bytes(int32_t op, int64_t T, int64_t H, int64_t V) {
   if (T < 0 || T > kMaxT || H <= 0 || H > kMaxH || H % 64 != 0 || V <= 0 || V > kMaxV) return 0;
   switch (op) {
     case RLK_OP_FWD:
-    case RLK_OP_PARTIAL: return fwd_layout(T, V).total;
+    case RLK_OP_PARTIAL: return fwd_layout(T, H, V).total;
     case RLK_OP_BWD: return bwd_layout(T, H, V).total;
     default: return 0;
   }
@@ -338,8 +344,8 @@ rlk_status rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* y, i
   if (!logp || !ws) return fail(RLK_ERR_NULL_ARG, "logp and ws are required");
   if (!aligned16(logp) || (lse && !aligned16(lse)) || !aligned16(ws))
     return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse, ws must be 16-byte aligned");
-  if (ws_bytes < fwd_layout(T, V).total)
-    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V).total, ws_bytes);
+  if (ws_bytes < fwd_layout(T, H, V).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, H, V).total, ws_bytes);
   RLK_TRY(check_device());
   RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
                       static_cast<hipStream_t>(stream)));
@@ -355,8 +361,8 @@ rlk_status rlk_lse_partial(const void* h, const void* W_shard, const int32_t* y,
   if (T == 0) return ok();
   if (!out || !ws) return fail(RLK_ERR_NULL_ARG, "out and ws are required");
   if (!aligned16(out) || !aligned16(ws)) return fail(RLK_ERR_BAD_ALIGNMENT, "out, ws must be 16-byte aligned");
-  if (ws_bytes < fwd_layout(T, V_global).total)
-    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, V_global).total, ws_bytes);
+  if (ws_bytes < fwd_layout(T, H, V_global).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, H, V_global).total, ws_bytes);
   RLK_TRY(check_device());
   RLK_TRY(run_forward(h, W_shard, y, T, H, V_global, ignore_index, s0, n, vocab_start, vocab_len, 1, nullptr, nullptr,
                       out, ws, static_cast<hipStream_t>(stream)));

@@ -76,30 +76,59 @@ __device__ __forceinline__ int slot_mn(int krow, int p) {
 }
 
 // ---- operand fragments from LDS ----------------------------------------------
-__device__ __forceinline__ bf16x8 frag_k(const u32x4* __restrict__ tile, int r0, int kk, int lane) {
-  const int row = r0 + (lane & 31);
-  const int seg = 2 * kk + (lane >> 5);
-  return __builtin_bit_cast(bf16x8, tile[slot_k(row, seg)]);
+// Per-lane LDS byte offsets of one operand's fragments within its tile,
+// computed once per tile so that every read in the main loop is a base
+// register plus an immediate:
+//   K mode : fragment J (rows r0 + 32 J ..) of k step kk at o[kk] + 4096 J
+//            (32 rows further keep the row's swizzle);
+//   MN mode: fragment J (columns r0 + 32 J ..) of k step kk: reads at
+//            o[J] + 8192 kk and o2[J] + 8192 kk (k-rows +16 keep the swizzle,
+//            k-rows +4 do not, hence two offsets).
+struct FragOffs {
+  uint32_t o[4], o2[4];
+};
+
+template <bool MN>
+__device__ __forceinline__ FragOffs frag_offs(int r0, int lane) {
+  FragOffs f;
+  if constexpr (!MN) {
+    const int row = r0 + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f.o[kk] = 16u * (uint32_t)slot_k(row, 2 * kk + (lane >> 5));
+      f.o2[kk] = 0u;
+    }
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int krow = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      const int col = r0 + 32 * J + 16 * (g & 1) + 4 * (s & 3);
+      const int p = col >> 3, half = (col >> 2) & 1;
+      f.o[J] = 16u * (uint32_t)slot_mn(krow, p) + 8u * half;
+      f.o2[J] = 16u * (uint32_t)slot_mn(krow + 4, p) + 8u * half;
+    }
+  }
+  return f;
 }
 
-__device__ __forceinline__ bf16x8 frag_mn(const u32x4* __restrict__ tile, int c0, int kk, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
-  const int p = col >> 3, half = (col >> 2) & 1;
-  const int krow = 16 * kk + 8 * (g >> 1) + (s >> 2);
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Fragment J, k step kk of the tile at `tile` (a pointer into the kernel's
+// LDS array: deriving every read from that array lets the compiler see that
+// reads of one stage do not alias the direct loads into the other one).
+template <bool MN, int J>
+__device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, int kk) {
   const char* base = reinterpret_cast<const char*>(tile);
-  const lds_bf16x4* p0 = (const lds_bf16x4*)(base + slot_mn(krow, p) * 16 + half * 8);
-  const lds_bf16x4* p1 = (const lds_bf16x4*)(base + slot_mn(krow + 4, p) * 16 + half * 8);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p0));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p1));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-template <bool A_MN>
-__device__ __forceinline__ bf16x8 frag_a(const u32x4* t, int r0, int kk, int lane) {
-  if constexpr (A_MN) return frag_mn(t, r0, kk, lane);
-  else return frag_k(t, r0, kk, lane);
+  if constexpr (!MN) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + f.o[kk] + 4096u * J));
+  } else {
+    const lds_bf16x4* p0 = (const lds_bf16x4*)(base + f.o[J] + 8192u * kk);
+    const lds_bf16x4* p1 = (const lds_bf16x4*)(base + f.o2[J] + 8192u * kk);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p0));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p1));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
 }
 
 // ---- global -> LDS staging (direct loads) ----------------------------------------
@@ -115,8 +144,18 @@ __device__ __forceinline__ bf16x8 frag_a(const u32x4* t, int r0, int kk, int lan
 // No registers hold the staged data.
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(const void* g, u32x4* tile, int slot0) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + slot0), 16, 0, 0);
+// Written as inline assembly (uniform base in scalar registers, 32-bit lane
+// offset): the compiler then does not know these loads write LDS, so it adds
+// no waits of its own before later LDS reads (it cannot tell the stages
+// apart for every read form).  The kernels order them explicitly: a stage is
+// read only after wait_vm and a barrier, and refilled only after a barrier
+// that follows the last reads of it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, u32x4* tile, int slot0) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(tile + slot0));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(off), "s"(base)
+               : "memory", "m0");
 }
 
 // K-mode row and piece of instruction i for this thread
@@ -130,39 +169,54 @@ __device__ __forceinline__ int dma_mn_piece(int krow) {
 }
 __device__ __forceinline__ int dma_slot0(int i) { return 64 * (kDma * (threadIdx.x >> 6) + i); }
 
-// K-mode loader over kDma rows whose pointers (with the piece offset) are
-// resolved once: pointer i is for row dma_k_row(i).
-struct RowsK8 {
-  const uint16_t* p[kDma];
+// Loaders keep one uniform base pointer (scalar registers) and, per lane,
+// 32-bit byte offsets of its kDma pieces (vector registers); the base moves
+// by one k-block per call.
+//
+// K-mode loader: tile row r is matrix row min(r, last) at base + row * ld
+// (bf16 elements).
+struct RowsK {
+  const char* base;
+  uint32_t off[kDma];
+  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
+    dma16(base + (size_t)kt * (2 * kBK), off[i], tile, dma_slot0(i));
+  }
   __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
-    const int o = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) dma16(p[i] + o, tile, dma_slot0(i));
+    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
   }
 };
 
-// K-mode rows r of a strided matrix (row pointer base + min(r, last) * ld)
-__device__ __forceinline__ RowsK8 rows_k_strided(const uint16_t* base, int last, int ld) {
-  RowsK8 R;
+__device__ __forceinline__ RowsK rows_k(const uint16_t* base, int last, int ld) {
+  RowsK R;
+  R.base = reinterpret_cast<const char*>(base);
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
     const int row = dma_k_row(i);
-    R.p[i] = base + (size_t)min(row, last) * ld + dma_k_seg(row) * 8;
+    R.off[i] = (uint32_t)(2 * ((size_t)min(row, last) * ld + dma_k_seg(row) * 8));
   }
   return R;
 }
 
-// K-mode rows gathered through idx: tile row r -> idx[min(first + r, n_last)]
-__device__ __forceinline__ RowsK8 rows_k_gather(const uint16_t* base, const int32_t* idx, int first, int n_last,
-                                               int ld) {
-  RowsK8 R;
-#pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int row = dma_k_row(i);
-    R.p[i] = base + (size_t)idx[min(first + row, n_last)] * ld + dma_k_seg(row) * 8;
+// ---- L2 prefetch -----------------------------------------------------------------
+// The tiles running together on one XCD share their operand rows, and the
+// first request for a line that is not yet in L2 stalls every tile waiting
+// for that k-block.  A tile therefore also pulls a share of the shared lines
+// of a later k-block into L2: one 4-byte direct load per lane (each loaded
+// line is whole in L2 afterwards) into an LDS word range that nothing reads.
+constexpr int kPfU4 = 16 * (kThreads / 64);  // 256 bytes of dump space per wave
+
+struct PrefetchK {
+  const uint16_t* p;  // this lane's line of k-block 0; k-block kt at p + kt * kBK
+  __device__ __forceinline__ void issue(int kt, u32x4* dump) const {
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(dump + 16 * (threadIdx.x >> 6)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(m0), "v"(p + (size_t)kt * kBK)
+                 : "memory", "m0");
   }
-  return R;
-}
+};
 
 // ---- main loop -------------------------------------------------------------------
 struct Acc {
@@ -173,93 +227,168 @@ struct Frags {
   bf16x8 a0, a1, a2, a3, b0, b1, b2, b3;
 };
 
-template <bool A_MN, bool B_MN>
-__device__ __forceinline__ void load_frags(const u32x4* __restrict__ sA, const u32x4* __restrict__ sB, int ra0,
-                                           int rb0, int kk, int lane, Frags& f) {
-  f.a0 = frag_a<A_MN>(sA, ra0, kk, lane);
-  f.a1 = frag_a<A_MN>(sA, ra0 + 32, kk, lane);
-  f.a2 = frag_a<A_MN>(sA, ra0 + 64, kk, lane);
-  f.a3 = frag_a<A_MN>(sA, ra0 + 96, kk, lane);
-  f.b0 = frag_a<B_MN>(sB, rb0, kk, lane);
-  f.b1 = frag_a<B_MN>(sB, rb0 + 32, kk, lane);
-  f.b2 = frag_a<B_MN>(sB, rb0 + 64, kk, lane);
-  f.b3 = frag_a<B_MN>(sB, rb0 + 96, kk, lane);
+// Fragment J of a set (0..3: A blocks, 4..7: B blocks), by compile-time index.
+template <int J>
+__device__ __forceinline__ bf16x8& frag(Frags& f) {
+  static_assert(J >= 0 && J < 8, "fragment index");
+  if constexpr (J == 0) return f.a0;
+  else if constexpr (J == 1) return f.a1;
+  else if constexpr (J == 2) return f.a2;
+  else if constexpr (J == 3) return f.a3;
+  else if constexpr (J == 4) return f.b0;
+  else if constexpr (J == 5) return f.b1;
+  else if constexpr (J == 6) return f.b2;
+  else return f.b3;
+}
+template <int J>
+__device__ __forceinline__ const bf16x8& frag(const Frags& f) {
+  return frag<J>(const_cast<Frags&>(f));
 }
 
-__device__ __forceinline__ void mma16(const Frags& f, Acc& acc) {
-#define RLK_MMA(mi, ni, A, B) acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.B, f.A, acc.c[mi][ni], 0, 0, 0);
-  RLK_MMA(0, 0, a0, b0) RLK_MMA(0, 1, a0, b1) RLK_MMA(0, 2, a0, b2) RLK_MMA(0, 3, a0, b3)
-  RLK_MMA(1, 0, a1, b0) RLK_MMA(1, 1, a1, b1) RLK_MMA(1, 2, a1, b2) RLK_MMA(1, 3, a1, b3)
-  RLK_MMA(2, 0, a2, b0) RLK_MMA(2, 1, a2, b1) RLK_MMA(2, 2, a2, b2) RLK_MMA(2, 3, a2, b3)
-  RLK_MMA(3, 0, a3, b0) RLK_MMA(3, 1, a3, b1) RLK_MMA(3, 2, a3, b2) RLK_MMA(3, 3, a3, b3)
-#undef RLK_MMA
+// Fragment J of k step kk (J < 4: A block J, else B block J - 4) from the
+// stage at LDS byte address st.
+template <bool A_MN, bool B_MN, int J>
+__device__ __forceinline__ void load_frag(const u32x4* st, const FragOffs& fa, const FragOffs& fb, int kk,
+                                          Frags& g) {
+  if constexpr (J < 4) frag<J>(g) = frag_at<A_MN, J>(st, fa, kk);
+  else frag<J>(g) = frag_at<B_MN, J - 4>(st + kTileU4, fb, kk);
+}
+
+template <bool A_MN, bool B_MN>
+__device__ __forceinline__ void load_frags(const u32x4* st, const FragOffs& fa, const FragOffs& fb, int kk,
+                                           Frags& g) {
+  load_frag<A_MN, B_MN, 0>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 1>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 2>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 3>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 4>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 5>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 6>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, 7>(st, fa, fb, kk, g);
+}
+
+// MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3).
+template <int J>
+__device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
+  constexpr int mi = J >> 2, ni = J & 3;
+  acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
+}
+
+// One k step: the 16 MFMAs on f, with the fragments of the next step (g, k
+// step kk of stage st) requested one per two MFMAs, or, with kDmaToo, all
+// requested first and then the direct loads of a later k-block (la/lb into
+// dA/dB) issued one per MFMA, so that neither the LDS nor the texture path
+// gets a burst the wave has to wait on.  (Reads placed after a direct load
+// into LDS would make the compiler wait for that load.)
+template <bool A_MN, bool B_MN, bool kLoadNext, bool kDmaToo, class LA, class LB>
+__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* st, const FragOffs& fa,
+                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, u32x4* dA,
+                                      u32x4* dB) {
+#define RLK_STEP(J)                                                                         \
+  if constexpr (kDmaToo) {                                                                  \
+    if constexpr ((J) < kDma) la.one((J), kb, dA);                                          \
+    else lb.one((J) - kDma, kb, dB);                                                        \
+  } else if constexpr (kLoadNext && (J) % 2 == 0) {                                         \
+    load_frag<A_MN, B_MN, (J) / 2>(st, fa, fb, kk, g);                                      \
+  }                                                                                         \
+  mma1<J>(f, acc);                                                                          \
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(2 * kDma == 16, "one direct load per MFMA");
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kDmaToo && kLoadNext) {
+    load_frags<A_MN, B_MN>(st, fa, fb, kk, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
+  RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
+#undef RLK_STEP
 }
 
 // Wait until at most n of this thread's vector memory operations are
 // outstanding (they complete in issue order, so everything older has landed).
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  if (n >= 2 * kDma + 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 static_assert(2 * kDma == 16, "wait_vm counts assume 16 direct loads per k-block");
 
-// nk k-blocks of kBK.  LA / LB: loaders with dma(kt, tile) that issue this
-// thread's direct global->LDS loads of k-block kt.  Two LDS stages: block kt
-// is read from stage kt & 1 while block kt+1 lands in the other one.  Per
-// k-block (four MFMA k steps of 16 MFMAs each):
-//   read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
-//   MFMAs step 2 | wait for block kt+1 and for this wave's reads, barrier,
-//   issue the loads of block kt+2 into stage kt & 1, read step 0 of block
-//   kt+1 | MFMAs step 3
-// so the one barrier per block sits between MFMA bursts, every LDS read
-// overlaps an MFMA burst, and after the barrier no wave reads stage kt & 1
-// any more.  Bare s_barrier: __syncthreads() would add a release fence that
-// waits for all outstanding loads, including the next block in flight.
-template <bool A_MN, bool B_MN, class LA, class LB>
-__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
+// Wait for all of this thread's LDS reads (s_waitcnt lgkmcnt(0) through the
+// builtin, which the compiler's own wait insertion takes into account).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// nk k-blocks of kBK.  LA / LB: loaders with one(i, kt, tile) / dma(kt,
+// tile) that issue this thread's direct global->LDS loads of k-block kt.
+// pf (optional, may be null): L2 prefetcher, issued right after the direct
+// loads of block b for block min(b + 2, nk - 1), so exactly one prefetch per
+// wave follows each block's loads.  lds: kLdsU4 stage words, then kPfU4 dump
+// words when prefetching.  Two LDS stages: block kt is read from stage kt & 1
+// while block kt+1 lands in the other one.  Per k-block (four MFMA k steps
+// of 16 MFMAs each, each step also requesting the next step's fragments):
+//   step 0 | step 1 | step 2 | wait for block kt+1 and for this wave's
+//   reads, barrier | step 3, which also issues the loads of block kt+2 into
+//   stage kt & 1 and reads step 0 of block kt+1
+// so the one barrier per block sits between MFMA bursts, and after it no
+// wave reads stage kt & 1 any more.  Bare s_barrier: __syncthreads() would
+// add a release fence that waits for all outstanding loads, including the
+// next block in flight.
+template <bool A_MN, bool B_MN, class LA, class LB, class PF = PrefetchK>
+__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds,
+                                        const PF* pf = nullptr) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = 128 * (w & 1), rb0 = 128 * (w >> 1);
   static_assert(kNS == 2 && kKK == 4, "schedule written for two stages of four k steps");
+  u32x4* dump = lds + kLdsU4;
   la.dma(0, lds);
   lb.dma(0, lds + kTileU4);
   if (nk > 1) {
+    if (pf) pf->issue(min(2, nk - 1), dump);
     la.dma(1, lds + kStageU4);
     lb.dma(1, lds + kStageU4 + kTileU4);
+    if (pf) pf->issue(min(3, nk - 1), dump);
   }
-  wait_vm(nk > 1 ? 2 * kDma : 0);
+  wait_vm(nk > 1 ? 2 * kDma + (pf ? 2 : 0) : 0);
   __builtin_amdgcn_s_barrier();
-  Frags f;
-  load_frags<A_MN, B_MN>(lds, lds + kTileU4, ra0, rb0, 0, lane, f);
-  for (int kt = 0; kt < nk; ++kt) {
-    const u32x4* sA = lds + (kt & 1) * kStageU4;
-    const u32x4* sB = sA + kTileU4;
-    Frags g;
+  const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
+  Frags f, g;
+  load_frags<A_MN, B_MN>(lds, fa, fb, 0, f);
+  // every block but the last: steps 1..3 requested during steps 0..2, then
+  // the barrier and step 3 with the next block's loads and first reads
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const u32x4* st = lds + (kt & 1) * kStageU4;
 #pragma unroll
     for (int kk = 1; kk < kKK; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_frags<A_MN, B_MN>(sA, sB, ra0, rb0, kk, lane, g);
-      __builtin_amdgcn_sched_barrier(0);
-      mma16(f, acc);
-      __builtin_amdgcn_sched_barrier(0);
+      // f has landed before g is requested: at most one step of reads is
+      // ever in flight, which the 4-bit LDS counter can track, so the
+      // MFMAs on f do not wait for g
+      wait_lds();
+      kstep<A_MN, B_MN, true, false>(f, g, acc, st, fa, fb, kk, la, lb, 0, nullptr, nullptr);
       f = g;
     }
-    if (kt + 1 < nk) {
-      wait_vm(0);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) {
-        u32x4* st = lds + (kt & 1) * kStageU4;
-        la.dma(kt + 2, st);
-        lb.dma(kt + 2, st + kTileU4);
-      }
-      const u32x4* nA = lds + ((kt + 1) & 1) * kStageU4;
-      load_frags<A_MN, B_MN>(nA, nA + kTileU4, ra0, rb0, 0, lane, g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(f, acc);
-    __builtin_amdgcn_sched_barrier(0);
+    // block kt+1 has landed and every wave is done with stage kt & 1:
+    // refill it with block kt+2 (the last block again when there is none,
+    // which keeps the load counts uniform; nothing reads that copy)
+    wait_vm(pf ? 1 : 0);
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    u32x4* sw = lds + (kt & 1) * kStageU4;
+    const u32x4* nx = lds + ((kt + 1) & 1) * kStageU4;
+    kstep<A_MN, B_MN, true, true>(f, g, acc, nx, fa, fb, 0, la, lb, min(kt + 2, nk - 1), sw, sw + kTileU4);
+    if (pf) pf->issue(min(kt + 4, nk - 1), dump);
     f = g;
+  }
+  {
+    const u32x4* st = lds + ((nk - 1) & 1) * kStageU4;
+#pragma unroll
+    for (int kk = 1; kk < kKK; ++kk) {
+      wait_lds();
+      kstep<A_MN, B_MN, true, false>(f, g, acc, st, fa, fb, kk, la, lb, 0, nullptr, nullptr);
+      f = g;
+    }
+    wait_lds();
+    kstep<A_MN, B_MN, false, false>(f, g, acc, st, fa, fb, 0, la, lb, 0, nullptr, nullptr);
   }
   __syncthreads();
 }

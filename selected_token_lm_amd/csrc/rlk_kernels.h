@@ -139,7 +139,7 @@ struct TileGeom {
 };
 
 struct FwdArgs {
-  const uint16_t* h;
+  const uint16_t* hA;  // active rows of h, compacted, zero padded to a multiple of 256
   const uint16_t* W;
   const int32_t* yA;  // targets of the active rows, compacted
   const int32_t* idx;
@@ -154,7 +154,7 @@ struct FwdArgs {
 };
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_tiles(FwdArgs a) {
-  __shared__ u32x4 lds[kLdsU4];
+  __shared__ u32x4 lds[kLdsU4 + kPfU4];
   const int id = xcd_tile(a.tg.per);
   if (id >= a.tg.row_tiles * a.nsplit * a.tg.tps) return;
   int rt, ct;
@@ -175,11 +175,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) tgt[mi] = a.yA[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
 
-  const RowsK8 A = rows_k_gather(a.h, a.idx, i0, n_act - 1, a.H);
-  const RowsK8 B = rows_k_strided(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
+  const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
+  const RowsK B = rows_k(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
+  // L2 prefetch shares: the 4 row tiles of a group split the W lines by
+  // row mod 4, the column tiles next to each other split the h lines by row
+  // mod 8 (waves 2 and 3 take residues 4 apart).  Two lanes per 128-byte line.
+  PrefetchK pf;
+  {
+    const int q = lane >> 1, half = 32 * (lane & 1);
+    if (w < 2) {
+      const int jr = 4 * (32 * w + q) + (rt & 3);
+      pf.p = a.W + (size_t)(c0 + min(jr, c1 - 1 - c0) - a.gm.vocab_start) * a.H + half;
+    } else {
+      const int ir = 8 * q + (((w == 2) ? ct : ct + 4) & 7);
+      pf.p = a.hA + (size_t)(i0 + ir) * a.H + half;
+    }
+  }
   Acc acc;
   acc_zero(acc);
-  gemm256<false, false>(A, B, a.H / kBK, acc, lds);
+  gemm256<false, false>(A, B, a.H / kBK, acc, lds, &pf);
 
   const int cc0 = c0 + kChunk * wn;  // this wave's chunk
   const int width = min(cc0 + kChunk, c1) - cc0;
@@ -363,7 +377,7 @@ struct DzArgs {
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
 // are written as zeros.  Each lane stores four consecutive columns (8 bytes).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dz_tiles(DzArgs a) {
-  __shared__ u32x4 lds[kLdsU4];
+  __shared__ u32x4 lds[kLdsU4 + kPfU4];
   const int id = xcd_tile(a.tg.per);
   if (id >= a.tg.row_tiles * a.bg.G * a.tg.tps) return;
   int rt, ct;
@@ -383,9 +397,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   Acc acc;
   acc_zero(acc);
   if (c0 < c1) {
-    const RowsK8 A = rows_k_strided(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
-    const RowsK8 B = rows_k_strided(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
-    gemm256<false, false>(A, B, a.H / kBK, acc, lds);
+    const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
+    const RowsK B = rows_k(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
+    PrefetchK pf;  // shares as in the forward
+    {
+      const int q = lane >> 1, half = 32 * (lane & 1);
+      if (w < 2) {
+        const int jr = 4 * (32 * w + q) + (rt & 3);
+        pf.p = a.W + (size_t)(c0 + min(jr, c1 - 1 - c0)) * a.H + half;
+      } else {
+        const int ir = 8 * q + (((w == 2) ? ct : ct + 4) & 7);
+        pf.p = a.hA + (size_t)(i0 + ir) * a.H + half;
+      }
+    }
+    gemm256<false, false>(A, B, a.H / kBK, acc, lds, &pf);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
 #pragma unroll
@@ -415,30 +440,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 // MN-mode loader over a row-major matrix: k-row t of k-block kt is matrix
-// row 64 kt + t at this tile's columns (dz columns for grad_W's A operand,
-// compacted hidden rows for its B operand).
+// row kBK kt + t at this tile's columns (dz columns for grad_W's A operand,
+// compacted hidden rows for its B operand).  base: matrix + first column of
+// the tile; off[i]: (k-row * ld + column of piece i) in bytes.
 struct ColsMN {
-  const uint16_t* col[kDma];  // matrix + column of piece i (row 0)
-  int ld;
+  const char* base;
+  uint32_t off[kDma];
+  size_t kstride;  // bytes per k-block
+  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
+    dma16(base + kt * kstride, off[i], tile, dma_slot0(i));
+  }
   __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) dma16(col[i] + (size_t)(kt * kBK + dma_mn_krow(i)) * ld, tile, dma_slot0(i));
+    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
   }
 };
 
+// Columns [c0, c0 + 256) of a row-major matrix with leading dimension ld,
+// piece columns clamped to ncol - 8.
+__device__ __forceinline__ ColsMN cols_mn(const uint16_t* m, int c0, int ncol, int ld) {
+  ColsMN L;
+  L.base = reinterpret_cast<const char*>(m + c0);
+  L.kstride = (size_t)2 * kBK * ld;
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int kr = dma_mn_krow(i);
+    const int col = min(c0 + dma_mn_piece(kr) * 8, ncol - 8) - c0;
+    L.off[i] = (uint32_t)(2 * ((size_t)kr * ld + col));
+  }
+  return L;
+}
+
 // MN-mode loader over the group's vocabulary rows of W: k index kg of the
 // group -> split sc = kg / S_pad, row (c_lo + sc) * S + kg % S_pad (clamped
-// to V - 1; those rows meet dz = 0).
+// to V - 1; those rows meet dz = 0).  A k-block never straddles two splits
+// (S_pad is a multiple of kBK).
 struct WRowsMN {
-  const uint16_t* col[kDma];  // W + column of piece i
+  const char* base;     // W + first column of the tile
+  uint32_t col2[kDma];  // byte offset of piece i's column
   int H, S, S_pad, c_lo, V;
-  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
     const int kg = kt * kBK;
     const int sc = kg / S_pad;
-    const int base = (c_lo + sc) * S + (kg - sc * S_pad);
+    const int r0 = min((c_lo + sc) * S + (kg - sc * S_pad), V - 1);
+    const int r = min((c_lo + sc) * S + (kg - sc * S_pad) + dma_mn_krow(i), V - 1);
+    dma16(base + (size_t)r0 * (2 * H), (uint32_t)((r - r0) * (2 * H)) + col2[i], tile, dma_slot0(i));
+  }
+  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
 #pragma unroll
-    for (int i = 0; i < kDma; ++i)
-      dma16(col[i] + (size_t)min(base + dma_mn_krow(i), V - 1) * H, tile, dma_slot0(i));
+    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
   }
 };
 
@@ -473,15 +523,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int n0 = nt * kBN;
   const int n_act = *a.n_act;
   const int tid = threadIdx.x;
-  ColsMN A, B;
-  A.ld = a.bg.ldz;
-  B.ld = a.H;
-#pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int p8 = dma_mn_piece(dma_mn_krow(i)) * 8;
-    A.col[i] = a.dZ + (size_t)sc * a.bg.S_pad + min(v0 + p8, a.bg.S_pad - 8);
-    B.col[i] = a.hA + min(n0 + p8, a.H - 8);
-  }
+  const ColsMN A = cols_mn(a.dZ + (size_t)sc * a.bg.S_pad, v0, a.bg.S_pad, a.bg.ldz);
+  const ColsMN B = cols_mn(a.hA, n0, a.H, a.H);
   Acc acc;
   acc_zero(acc);
   gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
@@ -562,15 +605,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const RowsK8 A = rows_k_strided(a.dZ + (size_t)i0 * a.bg.ldz, kBM - 1, a.bg.ldz);
+  const RowsK A = rows_k(a.dZ + (size_t)i0 * a.bg.ldz, kBM - 1, a.bg.ldz);
   WRowsMN B;
+  B.base = reinterpret_cast<const char*>(a.W + n0);
   B.H = a.H;
   B.S = a.gm.S;
   B.S_pad = a.bg.S_pad;
   B.c_lo = a.bg.c_lo;
   B.V = a.gm.V;
 #pragma unroll
-  for (int i = 0; i < kDma; ++i) B.col[i] = a.W + min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8);
+  for (int i = 0; i < kDma; ++i) B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
   gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
@@ -595,8 +639,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 
 // hA[i] = h[idx[i]] for active rows i < n_act, zero rows for n_act <= i <
-// rows; rowinfo[i] = {lse, g, target, 0} of the row ({0, 0, -1, 0} past
-// n_act).  grid rows, block 256; 16-byte pieces.
+// rows; rowinfo (optional) [i] = {lse, g, target, 0} of the row ({0, 0, -1,
+// 0} past n_act).  grid rows, block 256; 16-byte pieces.
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ n_act_p, int H,
                                                    const int32_t* __restrict__ y, const float* __restrict__ lse,
@@ -609,10 +653,10 @@ __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ 
     const int t = idx[i];
     const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)t * H);
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
-    if (threadIdx.x == 0) rowinfo[i] = make_float4(lse[t], g[t], __int_as_float(y[t]), 0.f);
+    if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(lse[t], g[t], __int_as_float(y[t]), 0.f);
   } else {
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
-    if (threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
+    if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
   }
 }
 
