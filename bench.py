@@ -41,10 +41,11 @@ WORKLOADS = {
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
 }
 
-# Kernels that carry the operator's MFMA work.  Each performs 2*T_act*H*V
-# algorithmic FLOPs per step (forward logits; backward recompute; grad_W;
-# grad_h), spread over its launches in that step.
-GEMM_KERNELS = ("fwd_tiles", "dz_tiles", "gradw_tiles", "gradh_tiles")
+# Kernels that carry the operator's MFMA work, with their algorithmic FLOPs
+# per step in units of 2*T_act*H*V (one contraction over the active rows):
+# forward logits; backward recompute; grad_h and grad_W (one launch), spread
+# over the kernel's launches in that step.
+GEMM_KERNELS = {"fwd_tiles": 1, "dz_tiles": 1, "grad_tiles": 2}
 
 
 def source_digest():
@@ -171,7 +172,7 @@ def main():
         avg = tot / n
         d = {"launches_per_step": n / args.steps, "avg_ms": avg, "ms_per_step": tot / args.steps}
         if name in GEMM_KERNELS:
-            d["flops_per_launch"] = per_step_flops / (n / args.steps)
+            d["flops_per_launch"] = GEMM_KERNELS[name] * per_step_flops / (n / args.steps)
             d["tflops"] = d["flops_per_launch"] / (avg * 1e-3) / 1e12
         kernels[name] = d
     dom = max((k for k in kernels if k in GEMM_KERNELS), key=lambda k: kernels[k]["ms_per_step"])

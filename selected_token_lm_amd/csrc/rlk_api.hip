@@ -150,6 +150,13 @@ rlk_status check_device() {
   return RLK_OK;
 }
 
+// Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension.
+rlk_status check_grid(int64_t blocks) {
+  if (blocks * rlk::kThreads > (int64_t)UINT32_MAX)
+    return fail(RLK_ERR_BAD_SHAPE, "problem needs %lld tile blocks, more than one launch holds", (long long)blocks);
+  return RLK_OK;
+}
+
 rlk_status launched(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RLK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -290,13 +297,13 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   fa.nsplit = nsplit;
   fa.gm = gm;
   fa.tg.tps = (int)ceil_div(g.S, rlk::kBN);
-  fa.tg.row_tiles = (int)ceil_div(T, rlk::kBM);
-  const int64_t ntiles = (int64_t)fa.tg.row_tiles * nsplit * fa.tg.tps;
-  fa.tg.per = (int)ceil_div(ntiles, 8);
   fa.rec_stride = (size_t)T;
   fa.rec = rec;
   fa.zt = zt;
-  RLK_LAUNCH(fwd_tiles, dim3((unsigned)(8 * fa.tg.per)), dim3(rlk::kThreads), st, fa);
+  // grid: every row tile of T (the kernel keeps those of active rows)
+  const int64_t fwd_blocks = 8 * ceil_div(ceil_div(T, rlk::kBM) * nsplit * fa.tg.tps, 8);
+  RLK_TRY(check_grid(fwd_blocks));
+  RLK_LAUNCH(fwd_tiles, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
 
   RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
              nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
@@ -425,9 +432,15 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
   for (int c = 0; c < rlk::kNSplit; ++c)
     if ((int64_t)c * gg.S < V) last_split = c;
   const int tps = (int)ceil_div(gg.S, rlk::kBN);
-  const int row_tiles = (int)ceil_div(T, rlk::kBM);
+  const int64_t row_tiles = ceil_div(T, rlk::kBM);
   const int n_tiles = (int)ceil_div(H, rlk::kBN);
   const int G = (int)L.G;
+  // grids: every row tile of T (the kernels keep those of active rows)
+  const int64_t dz_blocks = 8 * ceil_div(row_tiles * G * tps, 8);
+  const int64_t gh_blocks = grad_h ? 8 * ceil_div(row_tiles * n_tiles, 8) : 0;
+  const int64_t gw_blocks = grad_W ? 8 * ceil_div((int64_t)n_tiles * G * tps, 8) : 0;
+  RLK_TRY(check_grid(dz_blocks));
+  RLK_TRY(check_grid(gh_blocks + gw_blocks));
   for (int c_lo = 0; c_lo <= last_split; c_lo += G) {
     rlk::BwdGeom bg;
     bg.c_lo = c_lo;
@@ -444,46 +457,36 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
     da.H = (int)H;
     da.gm = gm;
     da.tg.tps = tps;
-    da.tg.row_tiles = row_tiles;
-    da.tg.per = (int)ceil_div((int64_t)row_tiles * G * tps, 8);
     da.bg = bg;
     da.dZ = dZ;
-    RLK_LAUNCH(dz_tiles, dim3((unsigned)(8 * da.tg.per)), dim3(rlk::kThreads), st, da);
+    RLK_LAUNCH(dz_tiles, dim3((unsigned)dz_blocks), dim3(rlk::kThreads), st, da);
 
-    if (grad_W) {
-      rlk::GradWArgs wa;
-      wa.dZ = dZ;
-      wa.hA = hA;
-      wa.idx = idx;
-      wa.n_act = n_act;
-      wa.H = (int)H;
-      wa.gm = gm;
-      wa.bg = bg;
-      wa.tps = tps;
-      wa.n_tiles = n_tiles;
-      wa.per = (int)ceil_div((int64_t)n_tiles * G * tps, 8);
-      wa.grad_W = grad_W;
-      RLK_LAUNCH(gradw_tiles, dim3((unsigned)(8 * wa.per)), dim3(rlk::kThreads), st, wa);
-    }
-    if (grad_h) {
-      rlk::GradHArgs ha;
-      ha.dZ = dZ;
-      ha.W = Wb;
-      ha.idx = idx;
-      ha.n_act = n_act;
-      ha.H = (int)H;
-      ha.gm = gm;
-      ha.bg = bg;
-      ha.n_tiles = n_tiles;
-      ha.row_tiles = row_tiles;
-      ha.per = (int)ceil_div((int64_t)n_tiles * row_tiles, 8);
-      ha.ghacc = ghacc;
-      ha.grad_h = static_cast<uint16_t*>(grad_h);
-      const bool first = c_lo == 0, last = c_lo + G > last_split;
-      void (*kfn)(rlk::GradHArgs) = first ? (last ? rlk::gradh_tiles<true, true> : rlk::gradh_tiles<true, false>)
-                                          : (last ? rlk::gradh_tiles<false, true> : rlk::gradh_tiles<false, false>);
-      RLK_LAUNCH_FN("gradh_tiles", kfn, dim3((unsigned)(8 * ha.per)), dim3(rlk::kThreads), st, ha);
-    }
+    rlk::GradWArgs wa;
+    wa.dZ = dZ;
+    wa.hA = hA;
+    wa.n_act = n_act;
+    wa.H = (int)H;
+    wa.gm = gm;
+    wa.bg = bg;
+    wa.tps = tps;
+    wa.n_tiles = n_tiles;
+    wa.grad_W = grad_W;
+    rlk::GradHArgs ha;
+    ha.dZ = dZ;
+    ha.W = Wb;
+    ha.idx = idx;
+    ha.n_act = n_act;
+    ha.H = (int)H;
+    ha.gm = gm;
+    ha.bg = bg;
+    ha.n_tiles = n_tiles;
+    ha.ghacc = ghacc;
+    ha.grad_h = static_cast<uint16_t*>(grad_h);
+    const bool first = c_lo == 0, last = c_lo + G > last_split;
+    void (*kfn)(rlk::GradHArgs, rlk::GradWArgs) =
+        first ? (last ? rlk::grad_tiles<true, true> : rlk::grad_tiles<true, false>)
+              : (last ? rlk::grad_tiles<false, true> : rlk::grad_tiles<false, false>);
+    RLK_LAUNCH_FN("grad_tiles", kfn, dim3((unsigned)(gh_blocks + gw_blocks)), dim3(rlk::kThreads), st, ha, wa);
   }
   return ok();
 }

@@ -198,26 +198,6 @@ __device__ __forceinline__ RowsK rows_k(const uint16_t* base, int last, int ld) 
   return R;
 }
 
-// ---- L2 prefetch -----------------------------------------------------------------
-// The tiles running together on one XCD share their operand rows, and the
-// first request for a line that is not yet in L2 stalls every tile waiting
-// for that k-block.  A tile therefore also pulls a share of the shared lines
-// of a later k-block into L2: one 4-byte direct load per lane (each loaded
-// line is whole in L2 afterwards) into an LDS word range that nothing reads.
-constexpr int kPfU4 = 16 * (kThreads / 64);  // 256 bytes of dump space per wave
-
-struct PrefetchK {
-  const uint16_t* p;  // this lane's line of k-block 0; k-block kt at p + kt * kBK
-  __device__ __forceinline__ void issue(int kt, u32x4* dump) const {
-    const uint32_t m0 =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(dump + 16 * (threadIdx.x >> 6)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(m0), "v"(p + (size_t)kt * kBK)
-                 : "memory", "m0");
-  }
-};
-
 // ---- main loop -------------------------------------------------------------------
 struct Acc {
   f32x16 c[kMI][kNI];
@@ -254,17 +234,24 @@ __device__ __forceinline__ void load_frag(const u32x4* st, const FragOffs& fa, c
   else frag<J>(g) = frag_at<B_MN, J - 4>(st + kTileU4, fb, kk);
 }
 
+// Fragment requested r-th (r = 0..7) for a k step: A0, B0, B1, B2, B3, A1,
+// A2, A3.  MFMA j of a step uses A (j >> 2) and B (j & 3), so with reads
+// completing in order the step's first MFMA waits for two reads only, and
+// each later read is needed at least 11 MFMAs after it is issued in the
+// step before.
+__device__ __forceinline__ constexpr int read_frag(int r) { return r == 0 ? 0 : (r <= 4 ? r + 3 : r - 4); }
+
 template <bool A_MN, bool B_MN>
 __device__ __forceinline__ void load_frags(const u32x4* st, const FragOffs& fa, const FragOffs& fb, int kk,
                                            Frags& g) {
-  load_frag<A_MN, B_MN, 0>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 1>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 2>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 3>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 4>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 5>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 6>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, 7>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(0)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(1)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(2)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(3)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(4)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(5)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(6)>(st, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(7)>(st, fa, fb, kk, g);
 }
 
 // MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3).
@@ -274,42 +261,10 @@ __device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
   acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
 }
 
-// One k step: the 16 MFMAs on f, with the fragments of the next step (g, k
-// step kk of stage st) requested one per two MFMAs, or, with kDmaToo, all
-// requested first and then the direct loads of a later k-block (la/lb into
-// dA/dB) issued one per MFMA, so that neither the LDS nor the texture path
-// gets a burst the wave has to wait on.  (Reads placed after a direct load
-// into LDS would make the compiler wait for that load.)
-template <bool A_MN, bool B_MN, bool kLoadNext, bool kDmaToo, class LA, class LB>
-__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* st, const FragOffs& fa,
-                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, u32x4* dA,
-                                      u32x4* dB) {
-#define RLK_STEP(J)                                                                         \
-  if constexpr (kDmaToo) {                                                                  \
-    if constexpr ((J) < kDma) la.one((J), kb, dA);                                          \
-    else lb.one((J) - kDma, kb, dB);                                                        \
-  } else if constexpr (kLoadNext && (J) % 2 == 0) {                                         \
-    load_frag<A_MN, B_MN, (J) / 2>(st, fa, fb, kk, g);                                      \
-  }                                                                                         \
-  mma1<J>(f, acc);                                                                          \
-  __builtin_amdgcn_sched_barrier(0);
-  static_assert(2 * kDma == 16, "one direct load per MFMA");
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kDmaToo && kLoadNext) {
-    load_frags<A_MN, B_MN>(st, fa, fb, kk, g);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
-  RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
-#undef RLK_STEP
-}
-
 // Wait until at most n of this thread's vector memory operations are
 // outstanding (they complete in issue order, so everything older has landed).
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 2 * kDma + 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 static_assert(2 * kDma == 16, "wait_vm counts assume 16 direct loads per k-block");
@@ -318,78 +273,105 @@ static_assert(2 * kDma == 16, "wait_vm counts assume 16 direct loads per k-block
 // builtin, which the compiler's own wait insertion takes into account).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// What a k step does besides its 16 MFMAs on f.
+enum StepKind {
+  kStepRead,   // request the next step's fragments (g, k step kk of stage st), one per two MFMAs
+  kStepSwap,   // last step of a k-block: 8 MFMAs; wait until k-block kt+1 has
+               // landed and this wave's reads are done; barrier; then per MFMA
+               // one fragment of the next block's first step (g, from st) and
+               // two direct loads of k-block kb (la/lb into dA/dB)
+  kStepLast,   // MFMAs only
+};
+
+// One k step.  No LDS wait is written for the fragment reads: before each
+// MFMA the compiler waits for exactly the reads it needs (LDS reads
+// complete in order).  In a kStepSwap step the barrier sits after the 8th
+// MFMA: by then every fragment of the block has long been read, so the
+// wait before it is short, and after it no wave reads the block's stage.
+// Bare s_barrier: __syncthreads() would add a release fence that waits for
+// all outstanding loads.
+template <bool A_MN, bool B_MN, StepKind kKind, class LA, class LB>
+__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* st, const FragOffs& fa,
+                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, u32x4* dA,
+                                      u32x4* dB) {
+#define RLK_STEP(J)                                                                              \
+  if constexpr (kKind == kStepRead && (J) % 2 == 0) {                                            \
+    load_frag<A_MN, B_MN, read_frag((J) / 2)>(st, fa, fb, kk, g);                                \
+  } else if constexpr (kKind == kStepSwap && (J) == 8) {                                         \
+    wait_vm(0);                                                                                  \
+    wait_lds();                                                                                  \
+    __builtin_amdgcn_s_barrier();                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+  }                                                                                              \
+  if constexpr (kKind == kStepSwap && (J) >= 8) {                                                \
+    load_frag<A_MN, B_MN, read_frag((J) - 8)>(st, fa, fb, 0, g);                                 \
+    if constexpr ((J) < 12) {                                                                    \
+      la.one(2 * ((J) - 8), kb, dA);                                                             \
+      la.one(2 * ((J) - 8) + 1, kb, dA);                                                         \
+    } else {                                                                                     \
+      lb.one(2 * ((J) - 12), kb, dB);                                                            \
+      lb.one(2 * ((J) - 12) + 1, kb, dB);                                                        \
+    }                                                                                            \
+  }                                                                                              \
+  mma1<J>(f, acc);                                                                               \
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(kDma == 8, "two direct loads per MFMA in the second half of a swap step");
+  __builtin_amdgcn_sched_barrier(0);
+  RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
+  RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
+#undef RLK_STEP
+}
+
 // nk k-blocks of kBK.  LA / LB: loaders with one(i, kt, tile) / dma(kt,
 // tile) that issue this thread's direct global->LDS loads of k-block kt.
-// pf (optional, may be null): L2 prefetcher, issued right after the direct
-// loads of block b for block min(b + 2, nk - 1), so exactly one prefetch per
-// wave follows each block's loads.  lds: kLdsU4 stage words, then kPfU4 dump
-// words when prefetching.  Two LDS stages: block kt is read from stage kt & 1
-// while block kt+1 lands in the other one.  Per k-block (four MFMA k steps
-// of 16 MFMAs each, each step also requesting the next step's fragments):
-//   step 0 | step 1 | step 2 | wait for block kt+1 and for this wave's
-//   reads, barrier | step 3, which also issues the loads of block kt+2 into
-//   stage kt & 1 and reads step 0 of block kt+1
-// so the one barrier per block sits between MFMA bursts, and after it no
-// wave reads stage kt & 1 any more.  Bare s_barrier: __syncthreads() would
-// add a release fence that waits for all outstanding loads, including the
-// next block in flight.
-template <bool A_MN, bool B_MN, class LA, class LB, class PF = PrefetchK>
-__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds,
-                                        const PF* pf = nullptr) {
+// lds: kLdsU4 words.  Two LDS stages: block kt is read from stage kt & 1
+// while block kt+1 lands in the other one.  Per k-block, four MFMA k steps
+// of 16 MFMAs each, each requesting the next step's fragments:
+//   step 0 | step 1 | step 2 | step 3: 8 MFMAs, wait for block kt+1,
+//   barrier, 8 MFMAs with the reads of block kt+1's step 0 and the loads
+//   of block kt+2 into stage kt & 1
+// The last block's loads are those of the last block again when there is
+// no block kt+2 (this keeps the load counts uniform; nothing reads that copy).
+template <bool A_MN, bool B_MN, class LA, class LB>
+__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = 128 * (w & 1), rb0 = 128 * (w >> 1);
   static_assert(kNS == 2 && kKK == 4, "schedule written for two stages of four k steps");
-  u32x4* dump = lds + kLdsU4;
   la.dma(0, lds);
   lb.dma(0, lds + kTileU4);
   if (nk > 1) {
-    if (pf) pf->issue(min(2, nk - 1), dump);
     la.dma(1, lds + kStageU4);
     lb.dma(1, lds + kStageU4 + kTileU4);
-    if (pf) pf->issue(min(3, nk - 1), dump);
   }
-  wait_vm(nk > 1 ? 2 * kDma + (pf ? 2 : 0) : 0);
+  wait_vm(nk > 1 ? 2 * kDma : 0);
   __builtin_amdgcn_s_barrier();
   const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
   Frags f, g;
   load_frags<A_MN, B_MN>(lds, fa, fb, 0, f);
-  // every block but the last: steps 1..3 requested during steps 0..2, then
-  // the barrier and step 3 with the next block's loads and first reads
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const u32x4* st = lds + (kt & 1) * kStageU4;
 #pragma unroll
-    for (int kk = 1; kk < kKK; ++kk) {
-      // f has landed before g is requested: at most one step of reads is
-      // ever in flight, which the 4-bit LDS counter can track, so the
-      // MFMAs on f do not wait for g
-      wait_lds();
-      kstep<A_MN, B_MN, true, false>(f, g, acc, st, fa, fb, kk, la, lb, 0, nullptr, nullptr);
+    for (int kk = 0; kk < kKK - 1; ++kk) {
+      kstep<A_MN, B_MN, kStepRead>(f, g, acc, st, fa, fb, kk + 1, la, lb, 0, nullptr, nullptr);
       f = g;
     }
-    // block kt+1 has landed and every wave is done with stage kt & 1:
-    // refill it with block kt+2 (the last block again when there is none,
-    // which keeps the load counts uniform; nothing reads that copy)
-    wait_vm(pf ? 1 : 0);
-    wait_lds();
-    __builtin_amdgcn_s_barrier();
     u32x4* sw = lds + (kt & 1) * kStageU4;
     const u32x4* nx = lds + ((kt + 1) & 1) * kStageU4;
-    kstep<A_MN, B_MN, true, true>(f, g, acc, nx, fa, fb, 0, la, lb, min(kt + 2, nk - 1), sw, sw + kTileU4);
-    if (pf) pf->issue(min(kt + 4, nk - 1), dump);
+    kstep<A_MN, B_MN, kStepSwap>(f, g, acc, nx, fa, fb, 0, la, lb, min(kt + 2, nk - 1), sw, sw + kTileU4);
     f = g;
   }
   {
     const u32x4* st = lds + ((nk - 1) & 1) * kStageU4;
 #pragma unroll
-    for (int kk = 1; kk < kKK; ++kk) {
-      wait_lds();
-      kstep<A_MN, B_MN, true, false>(f, g, acc, st, fa, fb, kk, la, lb, 0, nullptr, nullptr);
+    for (int kk = 0; kk < kKK - 1; ++kk) {
+      kstep<A_MN, B_MN, kStepRead>(f, g, acc, st, fa, fb, kk + 1, la, lb, 0, nullptr, nullptr);
       f = g;
     }
-    wait_lds();
-    kstep<A_MN, B_MN, false, false>(f, g, acc, st, fa, fb, 0, la, lb, 0, nullptr, nullptr);
+    kstep<A_MN, B_MN, kStepLast>(f, g, acc, st, fa, fb, 0, la, lb, 0, nullptr, nullptr);
   }
+  // every load issued has landed and every wave is done with the stages
+  wait_vm(0);
   __syncthreads();
 }
 
@@ -410,12 +392,18 @@ __device__ __forceinline__ int acc_col4(int wn, int ni, int g, int lane) {
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Give XCD x the contiguous range [x*per, (x+1)*per) of tile ids so
-// that the tiles running together on one XCD share operand rows in its L2.
-// The grid must hold 8*per blocks; ids >= the tile count exit.
-__device__ __forceinline__ int xcd_tile(int per) {
-  const int bid = blockIdx.x;
-  return (bid & 7) * per + (bid >> 3);
+// L2): block b runs on XCD b mod 8.  With `live` tiles to run (a count the
+// device may only know at run time, such as the active-row tiles), XCD x
+// takes the contiguous id range [x*per, (x+1)*per), per = ceil(live / 8):
+// the tiles running together on one XCD share operand rows in its L2, and
+// every XCD gets the same number of tiles.  Returns -1 for blocks beyond the
+// live tiles (grids are sized for the largest possible count).
+__device__ __forceinline__ int xcd_tile(int live, int bid) {
+  const int per = (live + 7) >> 3;
+  const int slot = bid >> 3;
+  if (slot >= per) return -1;
+  const int id = (bid & 7) * per + slot;
+  return id < live ? id : -1;
 }
 
 // Tile id -> (fast index f < F, slow index c < C) in groups of GM fast

@@ -7,8 +7,9 @@
 //   merge_parts        tree over per-range statistics (rlk_lse_merge)
 // Backward (per group of vocabulary splits, ascending):
 //   dz_tiles           recomputed logits -> dz = g (onehot - softmax), bf16
-//   gradw_tiles        grad_W rows of the group = dz^T h  (K = active rows)
-//   gradh_tiles        fp32 accumulator += dz W; bf16 after the last group
+//   grad_tiles         one launch of the group's tiles of
+//                        grad_h: fp32 accumulator += dz W; bf16 after the last group
+//                        grad_W: rows of the group = dz^T h  (K = active rows)
 //   zero_rows          zero grad_h rows of inactive rows
 #pragma once
 
@@ -133,9 +134,7 @@ __device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
 //         the half's 64 columns in ascending order.
 // ---------------------------------------------------------------------------
 struct TileGeom {
-  int tps;        // 256-column tiles per split = ceil(S / 256)
-  int row_tiles;  // 256-row tiles covering T
-  int per;        // tiles per XCD (grid = 8 * per)
+  int tps;  // 256-column tiles per split = ceil(S / 256)
 };
 
 struct FwdArgs {
@@ -154,14 +153,17 @@ struct FwdArgs {
 };
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_tiles(FwdArgs a) {
-  __shared__ u32x4 lds[kLdsU4 + kPfU4];
-  const int id = xcd_tile(a.tg.per);
-  if (id >= a.tg.row_tiles * a.nsplit * a.tg.tps) return;
+  __shared__ u32x4 lds[kLdsU4];
+  // tiles: the active-row tiles x every 256-column tile of the range (the
+  // count goes through a scalar register: tile addresses derive from it)
+  const int n_act = __builtin_amdgcn_readfirstlane(*a.n_act);
+  const int rtiles = (n_act + kBM - 1) / kBM;
+  const int C = a.nsplit * a.tg.tps;
+  const int id = xcd_tile(rtiles * C, blockIdx.x);
+  if (id < 0) return;
   int rt, ct;
-  grouped_tile(id, a.tg.row_tiles, rt, ct, a.nsplit * a.tg.tps);
-  const int n_act = *a.n_act;
+  grouped_tile(id, rtiles, rt, ct, C);
   const int i0 = rt * kBM;
-  if (i0 >= n_act) return;
   const int sl = ct / a.tg.tps, j = ct - sl * a.tg.tps;
   const int sbeg = (a.gm.s0 + sl) * a.gm.S;
   const int send = min(sbeg + a.gm.S, a.gm.V);
@@ -177,23 +179,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
   const RowsK B = rows_k(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
-  // L2 prefetch shares: the 4 row tiles of a group split the W lines by
-  // row mod 4, the column tiles next to each other split the h lines by row
-  // mod 8 (waves 2 and 3 take residues 4 apart).  Two lanes per 128-byte line.
-  PrefetchK pf;
-  {
-    const int q = lane >> 1, half = 32 * (lane & 1);
-    if (w < 2) {
-      const int jr = 4 * (32 * w + q) + (rt & 3);
-      pf.p = a.W + (size_t)(c0 + min(jr, c1 - 1 - c0) - a.gm.vocab_start) * a.H + half;
-    } else {
-      const int ir = 8 * q + (((w == 2) ? ct : ct + 4) & 7);
-      pf.p = a.hA + (size_t)(i0 + ir) * a.H + half;
-    }
-  }
   Acc acc;
   acc_zero(acc);
-  gemm256<false, false>(A, B, a.H / kBK, acc, lds, &pf);
+  gemm256<false, false>(A, B, a.H / kBK, acc, lds);
 
   const int cc0 = c0 + kChunk * wn;  // this wave's chunk
   const int width = min(cc0 + kChunk, c1) - cc0;
@@ -377,14 +365,15 @@ struct DzArgs {
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
 // are written as zeros.  Each lane stores four consecutive columns (8 bytes).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dz_tiles(DzArgs a) {
-  __shared__ u32x4 lds[kLdsU4 + kPfU4];
-  const int id = xcd_tile(a.tg.per);
-  if (id >= a.tg.row_tiles * a.bg.G * a.tg.tps) return;
+  __shared__ u32x4 lds[kLdsU4];
+  const int n_act = __builtin_amdgcn_readfirstlane(*a.n_act);
+  const int rtiles = (n_act + kBM - 1) / kBM;
+  const int C = a.bg.G * a.tg.tps;
+  const int id = xcd_tile(rtiles * C, blockIdx.x);
+  if (id < 0) return;
   int rt, ct;
-  grouped_tile(id, a.tg.row_tiles, rt, ct, a.bg.G * a.tg.tps);
-  const int n_act = *a.n_act;
+  grouped_tile(id, rtiles, rt, ct, C);
   const int i0 = rt * kBM;
-  if (i0 >= n_act) return;
   const int sc = ct / a.tg.tps, j = ct - sc * a.tg.tps;
   const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));  // columns of this split
@@ -399,18 +388,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (c0 < c1) {
     const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
     const RowsK B = rows_k(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
-    PrefetchK pf;  // shares as in the forward
-    {
-      const int q = lane >> 1, half = 32 * (lane & 1);
-      if (w < 2) {
-        const int jr = 4 * (32 * w + q) + (rt & 3);
-        pf.p = a.W + (size_t)(c0 + min(jr, c1 - 1 - c0)) * a.H + half;
-      } else {
-        const int ir = 8 * q + (((w == 2) ? ct : ct + 4) & 7);
-        pf.p = a.hA + (size_t)(i0 + ir) * a.H + half;
-      }
-    }
-    gemm256<false, false>(A, B, a.H / kBK, acc, lds, &pf);
+    gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
 #pragma unroll
@@ -495,24 +473,19 @@ struct WRowsMN {
 struct GradWArgs {
   const uint16_t* dZ;
   const uint16_t* hA;  // active rows of h, compacted, zero padded to T_pad
-  const int32_t* idx;
   const int32_t* n_act;
   int H;
   SplitGeom gm;
   BwdGeom bg;
   int tps;      // 256-row v tiles per split
   int n_tiles;  // 256-column tiles of H
-  int per;
-  float* grad_W;
+  float* grad_W;  // NULL: not wanted
 };
 
 // grad_W rows of the group's splits: C[v][n] = sum_t dz[t][v] h[t][n], the
 // chain over active rows t ascending (K padded to 64 with zero dz rows).
-// Both operands are MN mode.  Written once, fp32.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gradw_tiles(GradWArgs a) {
-  __shared__ u32x4 lds[kLdsU4];
-  const int id = xcd_tile(a.per);
-  if (id >= a.n_tiles * a.bg.G * a.tps) return;
+// Both operands are MN mode.  Written once, fp32.  Tile id: (H tile, v tile).
+__device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4* lds) {
   int nt, vt;
   grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps);
   const int sc = vt / a.tps, j = vt - sc * a.tps;
@@ -521,7 +494,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int v0 = j * kBM;  // within the split
   if (v0 >= valid_s) return;
   const int n0 = nt * kBN;
-  const int n_act = *a.n_act;
   const int tid = threadIdx.x;
   const ColsMN A = cols_mn(a.dZ + (size_t)sc * a.bg.S_pad, v0, a.bg.S_pad, a.bg.ldz);
   const ColsMN B = cols_mn(a.hA, n0, a.H, a.H);
@@ -554,11 +526,9 @@ struct GradHArgs {
   int H;
   SplitGeom gm;
   BwdGeom bg;
-  int n_tiles;    // 256-column tiles of H
-  int row_tiles;  // 256-row tiles covering T
-  int per;
+  int n_tiles;  // 256-column tiles of H
   float* ghacc;
-  uint16_t* grad_h;
+  uint16_t* grad_h;  // NULL: not wanted
 };
 
 // grad_h of the group: acc[i][n] (+)= sum_v dz[i][v] W[v][n] over the
@@ -566,17 +536,12 @@ struct GradHArgs {
 // fp32 chain continues across groups through ghacc (exact store/load); after
 // the last group it is rounded to bf16 once and written to the row's place.
 // kFirst / kLast: the group is the first / last one (compile-time, so that
-// the accumulators never merge across a branch).
+// the accumulators never merge across a branch).  Tile id: (row tile, H tile).
 template <bool kFirst, bool kLast>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gradh_tiles(GradHArgs a) {
-  __shared__ u32x4 lds[kLdsU4];
-  const int id = xcd_tile(a.per);
-  if (id >= a.n_tiles * a.row_tiles) return;
+__device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int n_act, u32x4* lds) {
   int rt, nt;
-  grouped_tile(id, a.row_tiles, rt, nt, a.n_tiles);
-  const int n_act = *a.n_act;
+  grouped_tile(id, rtiles, rt, nt, a.n_tiles);
   const int i0 = rt * kBM, n0 = nt * kBN;
-  if (i0 >= n_act) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
   int dst[kMI];  // output rows of this lane's active rows, loaded ahead
   if (kLast) {
@@ -635,6 +600,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
               make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
       }
   }
+}
+
+// The group's grad_h and grad_W tiles in one launch.  The grad_h tiles
+// (K = the group's whole padded vocabulary, few of them) take the first
+// blocks and start first; the grad_W tiles (K = active rows, many short
+// ones) follow and fill the compute units that the grad_h tiles leave free,
+// then all of them as the grad_h tiles finish.  Either part is skipped when
+// its output pointer is NULL.
+template <bool kFirst, bool kLast>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_tiles(GradHArgs ha,
+                                                                                               GradWArgs wa) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int n_act = __builtin_amdgcn_readfirstlane(*ha.n_act);
+  const int rtiles = (n_act + kBM - 1) / kBM;
+  const int nh = ha.grad_h ? rtiles * ha.n_tiles : 0;
+  const int nh_blocks = 8 * ((nh + 7) >> 3);
+  const int bid = blockIdx.x;
+  if (bid < nh_blocks) {
+    const int id = xcd_tile(nh, bid);
+    if (id >= 0) gradh_tile<kFirst, kLast>(ha, id, rtiles, n_act, lds);
+    return;
+  }
+  // nh_blocks is a multiple of 8: block bid - nh_blocks runs on the same XCD
+  const int nw = wa.grad_W ? wa.n_tiles * wa.bg.G * wa.tps : 0;
+  const int id = xcd_tile(nw, bid - nh_blocks);
+  if (id >= 0) gradw_tile(wa, id, n_act, lds);
 }
 
 
