@@ -60,9 +60,8 @@ constexpr int kDma = kBK / 8;              // direct-load instructions per wave 
 constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (32 KB)
 constexpr int kTileU4Check = 256 * kBK / 8;
 static_assert(kTileU4 == kTileU4Check, "tile = 256 rows x kBK bf16");
-constexpr int kStageU4 = 2 * kTileU4;      // A + B (64 KB)
-constexpr int kNS = 2;                     // LDS stages
-constexpr int kLdsU4 = kNS * kStageU4;     // 128 KB
+constexpr int kSlots = 5;                  // LDS tile slots (a ring of operand tiles)
+constexpr int kLdsU4 = kSlots * kTileU4;   // 160 KB, all of a CU's LDS
 
 // K-mode slot of (row, 16-byte piece seg), 128-byte rows: two consecutive
 // rows fill a 256-byte bank row and the piece index is xor-ed with
@@ -150,8 +149,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // apart for every read form).  The kernels order them explicitly: a stage is
 // read only after wait_vm and a barrier, and refilled only after a barrier
 // that follows the last reads of it.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, u32x4* tile, int slot0) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(tile + slot0));
+// m0: LDS byte address of the instruction's 1 KB (wave-uniform).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(m0), "v"(off), "s"(base)
@@ -167,23 +166,32 @@ __device__ __forceinline__ int dma_mn_piece(int krow) {
   const int l = threadIdx.x & 31;
   return (((l >> 2) ^ (krow & 7)) << 2) | (l & 3);
 }
-__device__ __forceinline__ int dma_slot0(int i) { return 64 * (kDma * (threadIdx.x >> 6) + i); }
+// LDS byte address of this wave's first direct-load slot in the tile at
+// LDS byte address t (instruction i then writes 1 KB further per i).
+__device__ __forceinline__ uint32_t dma_wave_base(uint32_t t) {
+  return t + 1024u * kDma * (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+// LDS byte address of a tile given as a pointer into the kernel's LDS array.
+__device__ __forceinline__ uint32_t lds_addr(const u32x4* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
 
 // Loaders keep one uniform base pointer (scalar registers) and, per lane,
 // 32-bit byte offsets of its kDma pieces (vector registers); the base moves
-// by one k-block per call.
+// by one k-block per call.  one(i, kt, m0w) issues instruction i of k-block
+// kt into the tile whose wave slot base is m0w (dma_wave_base).
 //
 // K-mode loader: tile row r is matrix row min(r, last) at base + row * ld
 // (bf16 elements).
 struct RowsK {
   const char* base;
   uint32_t off[kDma];
-  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
-    dma16(base + (size_t)kt * (2 * kBK), off[i], tile, dma_slot0(i));
+  __device__ __forceinline__ void one(int i, int kt, uint32_t m0w) const {
+    dma16(base + (size_t)kt * (2 * kBK), off[i], m0w + 1024u * i);
   }
-  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+  __device__ __forceinline__ void dma(int kt, uint32_t m0w) const {
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
+    for (int i = 0; i < kDma; ++i) one(i, kt, m0w);
   }
 };
 
@@ -227,11 +235,12 @@ __device__ __forceinline__ const bf16x8& frag(const Frags& f) {
 
 // Fragment J of k step kk (J < 4: A block J, else B block J - 4) from the
 // stage at LDS byte address st.
+// (tA, tB: the k-block's A and B tiles in LDS.)
 template <bool A_MN, bool B_MN, int J>
-__device__ __forceinline__ void load_frag(const u32x4* st, const FragOffs& fa, const FragOffs& fb, int kk,
-                                          Frags& g) {
-  if constexpr (J < 4) frag<J>(g) = frag_at<A_MN, J>(st, fa, kk);
-  else frag<J>(g) = frag_at<B_MN, J - 4>(st + kTileU4, fb, kk);
+__device__ __forceinline__ void load_frag(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
+                                          int kk, Frags& g) {
+  if constexpr (J < 4) frag<J>(g) = frag_at<A_MN, J>(tA, fa, kk);
+  else frag<J>(g) = frag_at<B_MN, J - 4>(tB, fb, kk);
 }
 
 // Fragment requested r-th (r = 0..7) for a k step: A0, B0, B1, B2, B3, A1,
@@ -242,16 +251,16 @@ __device__ __forceinline__ void load_frag(const u32x4* st, const FragOffs& fa, c
 __device__ __forceinline__ constexpr int read_frag(int r) { return r == 0 ? 0 : (r <= 4 ? r + 3 : r - 4); }
 
 template <bool A_MN, bool B_MN>
-__device__ __forceinline__ void load_frags(const u32x4* st, const FragOffs& fa, const FragOffs& fb, int kk,
-                                           Frags& g) {
-  load_frag<A_MN, B_MN, read_frag(0)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(1)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(2)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(3)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(4)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(5)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(6)>(st, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(7)>(st, fa, fb, kk, g);
+__device__ __forceinline__ void load_frags(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
+                                           int kk, Frags& g) {
+  load_frag<A_MN, B_MN, read_frag(0)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(1)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(2)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(3)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(4)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(5)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(6)>(tA, tB, fa, fb, kk, g);
+  load_frag<A_MN, B_MN, read_frag(7)>(tA, tB, fa, fb, kk, g);
 }
 
 // MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3).
@@ -261,13 +270,14 @@ __device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
   acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
 }
 
-// Wait until at most n of this thread's vector memory operations are
-// outstanding (they complete in issue order, so everything older has landed).
+// Wait until at most n (0 or 8) of this thread's vector memory operations
+// are outstanding (they complete in issue order, so everything older has
+// landed).
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 2 * kDma) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  if (n >= kDma) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-static_assert(2 * kDma == 16, "wait_vm counts assume 16 direct loads per k-block");
+static_assert(kDma == 8, "wait_vm counts assume 8 direct loads per operand tile");
 
 // Wait for all of this thread's LDS reads (s_waitcnt lgkmcnt(0) through the
 // builtin, which the compiler's own wait insertion takes into account).
@@ -275,11 +285,13 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 // What a k step does besides its 16 MFMAs on f.
 enum StepKind {
-  kStepRead,   // request the next step's fragments (g, k step kk of stage st), one per two MFMAs
-  kStepSwap,   // last step of a k-block: 8 MFMAs; wait until k-block kt+1 has
-               // landed and this wave's reads are done; barrier; then per MFMA
-               // one fragment of the next block's first step (g, from st) and
-               // two direct loads of k-block kb (la/lb into dA/dB)
+  kStepRead,   // request the next step's fragments (g: k step kk of tiles tA, tB), one per two
+               // MFMAs; with kDmaB also direct loads 4 kB0 .. 4 kB0 + 3 of a B tile (lb, k-block
+               // kb, wave slot base dB), one per four MFMAs
+  kStepSwap,   // last step of a k-block: 8 MFMAs; wait until the next k-block has landed and
+               // this wave's reads are done; barrier; then per MFMA one fragment of the next
+               // block's first step (g from tA, tB) and one direct load of an A tile (la, k-block
+               // kb, wave slot base dA)
   kStepLast,   // MFMAs only
 };
 
@@ -287,90 +299,105 @@ enum StepKind {
 // MFMA the compiler waits for exactly the reads it needs (LDS reads
 // complete in order).  In a kStepSwap step the barrier sits after the 8th
 // MFMA: by then every fragment of the block has long been read, so the
-// wait before it is short, and after it no wave reads the block's stage.
+// wait before it is short, and after it no wave reads the block's tiles.
 // Bare s_barrier: __syncthreads() would add a release fence that waits for
-// all outstanding loads.
-template <bool A_MN, bool B_MN, StepKind kKind, class LA, class LB>
-__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* st, const FragOffs& fa,
-                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, u32x4* dA,
-                                      u32x4* dB) {
+// all outstanding loads.  Direct loads are spread one per one to four MFMAs
+// so that the address path never backs up into the wave's in-order issue.
+template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB = false, int kB0 = 0, class LA, class LB>
+__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* tA, const u32x4* tB,
+                                      const FragOffs& fa, const FragOffs& fb, int kk, const LA& la, const LB& lb,
+                                      int kb, uint32_t dA, uint32_t dB) {
 #define RLK_STEP(J)                                                                              \
   if constexpr (kKind == kStepRead && (J) % 2 == 0) {                                            \
-    load_frag<A_MN, B_MN, read_frag((J) / 2)>(st, fa, fb, kk, g);                                \
+    load_frag<A_MN, B_MN, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                            \
+  } else if constexpr (kKind == kStepRead && kDmaB && (J) % 4 == 1) {                            \
+    lb.one(4 * kB0 + (J) / 4, kb, dB);                                                           \
   } else if constexpr (kKind == kStepSwap && (J) == 8) {                                         \
-    wait_vm(0);                                                                                  \
+    wait_vm(kDma);                                                                               \
     wait_lds();                                                                                  \
     __builtin_amdgcn_s_barrier();                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                           \
   }                                                                                              \
   if constexpr (kKind == kStepSwap && (J) >= 8) {                                                \
-    load_frag<A_MN, B_MN, read_frag((J) - 8)>(st, fa, fb, 0, g);                                 \
-    if constexpr ((J) < 12) {                                                                    \
-      la.one(2 * ((J) - 8), kb, dA);                                                             \
-      la.one(2 * ((J) - 8) + 1, kb, dA);                                                         \
-    } else {                                                                                     \
-      lb.one(2 * ((J) - 12), kb, dB);                                                            \
-      lb.one(2 * ((J) - 12) + 1, kb, dB);                                                        \
-    }                                                                                            \
+    load_frag<A_MN, B_MN, read_frag((J) - 8)>(tA, tB, fa, fb, 0, g);                             \
+    la.one((J) - 8, kb, dA);                                                                     \
   }                                                                                              \
   mma1<J>(f, acc);                                                                               \
   __builtin_amdgcn_sched_barrier(0);
-  static_assert(kDma == 8, "two direct loads per MFMA in the second half of a swap step");
+  static_assert(kDma == 8, "one direct load per MFMA in the second half of a swap step");
   __builtin_amdgcn_sched_barrier(0);
   RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
   RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
 #undef RLK_STEP
 }
 
-// nk k-blocks of kBK.  LA / LB: loaders with one(i, kt, tile) / dma(kt,
-// tile) that issue this thread's direct global->LDS loads of k-block kt.
-// lds: kLdsU4 words.  Two LDS stages: block kt is read from stage kt & 1
-// while block kt+1 lands in the other one.  Per k-block, four MFMA k steps
-// of 16 MFMAs each, each requesting the next step's fragments:
-//   step 0 | step 1 | step 2 | step 3: 8 MFMAs, wait for block kt+1,
-//   barrier, 8 MFMAs with the reads of block kt+1's step 0 and the loads
-//   of block kt+2 into stage kt & 1
-// The last block's loads are those of the last block again when there is
-// no block kt+2 (this keeps the load counts uniform; nothing reads that copy).
+// nk k-blocks of kBK.  LA / LB: loaders with one(i, kt, m0w) / dma(kt, m0w)
+// that issue this thread's direct global->LDS loads of k-block kt.  lds:
+// kLdsU4 words = a ring of 5 operand-tile slots.  Tile q = 2 kt (B of block
+// kt) or 2 kt + 1 (A of block kt) lives in slot q mod 5, so at any time the
+// ring holds the two tiles being read, the next block's two and one more.
+// Per k-block kt, four MFMA k steps of 16 MFMAs each, each requesting the
+// next step's fragments:
+//   step 0 | step 1     (with the loads of B of block kt+2, 1 per 4 MFMAs)
+//   step 2 | step 3: 8 MFMAs, wait for block kt+1, barrier, 8 MFMAs with
+//   the reads of block kt+1's step 0 and the loads of A of block kt+2
+// so B tiles are issued about 1.5 blocks and A tiles 1 block before use.
+// Loads past the last block repeat the last block's tile into the free slot
+// (uniform load counts; nothing reads that copy); all have landed on return.
 template <bool A_MN, bool B_MN, class LA, class LB>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = 128 * (w & 1), rb0 = 128 * (w >> 1);
-  static_assert(kNS == 2 && kKK == 4, "schedule written for two stages of four k steps");
-  la.dma(0, lds);
-  lb.dma(0, lds + kTileU4);
-  if (nk > 1) {
-    la.dma(1, lds + kStageU4);
-    lb.dma(1, lds + kStageU4 + kTileU4);
-  }
-  wait_vm(nk > 1 ? 2 * kDma : 0);
+  static_assert(kKK == 4 && kSlots == 5, "schedule written for four k steps and five tile slots");
+  // direct-load slot base of this wave in slot 0; slot s is kTileB * s further
+  const uint32_t m0s = dma_wave_base(lds_addr(lds));
+  constexpr uint32_t kTileB = 16u * kTileU4;
+  // prologue: B0, A0 (slots 0, 1), then B1, A1 (slots 2, 3)
+  lb.dma(0, m0s);
+  la.dma(0, m0s + kTileB);
+  const int k1 = min(1, nk - 1);
+  lb.dma(k1, m0s + 2 * kTileB);
+  la.dma(k1, m0s + 3 * kTileB);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // B0 and A0 have landed
   __builtin_amdgcn_s_barrier();
   const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
   Frags f, g;
-  load_frags<A_MN, B_MN>(lds, fa, fb, 0, f);
+  int sb = 0;  // slot of B of the current block (A is in slot sb + 1 mod 5)
+  load_frags<A_MN, B_MN>(lds + kTileU4, lds, fa, fb, 0, f);
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    const u32x4* st = lds + (kt & 1) * kStageU4;
-#pragma unroll
-    for (int kk = 0; kk < kKK - 1; ++kk) {
-      kstep<A_MN, B_MN, kStepRead>(f, g, acc, st, fa, fb, kk + 1, la, lb, 0, nullptr, nullptr);
-      f = g;
-    }
-    u32x4* sw = lds + (kt & 1) * kStageU4;
-    const u32x4* nx = lds + ((kt + 1) & 1) * kStageU4;
-    kstep<A_MN, B_MN, kStepSwap>(f, g, acc, nx, fa, fb, 0, la, lb, min(kt + 2, nk - 1), sw, sw + kTileU4);
+    const int sa = sb == 4 ? 0 : sb + 1;
+    const u32x4* tA = lds + sa * kTileU4;
+    const u32x4* tB = lds + sb * kTileU4;
+    // block kt+2: B into slot (sb + 4) mod 5 (freed by A of block kt-1), A into
+    // slot sb (freed by B of block kt at this block's barrier)
+    const int k2 = min(kt + 2, nk - 1);
+    const int sb2 = sb == 0 ? 4 : sb - 1;
+    kstep<A_MN, B_MN, kStepRead, true, 0>(f, g, acc, tA, tB, fa, fb, 1, la, lb, k2, 0u, m0s + sb2 * kTileB);
     f = g;
+    kstep<A_MN, B_MN, kStepRead, true, 1>(f, g, acc, tA, tB, fa, fb, 2, la, lb, k2, 0u, m0s + sb2 * kTileB);
+    f = g;
+    kstep<A_MN, B_MN, kStepRead>(f, g, acc, tA, tB, fa, fb, 3, la, lb, 0, 0u, 0u);
+    f = g;
+    const int sbn = sb >= 3 ? sb - 3 : sb + 2;  // slot of B of block kt+1
+    const int san = sbn == 4 ? 0 : sbn + 1;
+    kstep<A_MN, B_MN, kStepSwap>(f, g, acc, lds + san * kTileU4, lds + sbn * kTileU4, fa, fb, 0, la, lb, k2,
+                                 m0s + sb * kTileB, 0u);
+    f = g;
+    sb = sbn;
   }
   {
-    const u32x4* st = lds + ((nk - 1) & 1) * kStageU4;
+    const int sa = sb == 4 ? 0 : sb + 1;
+    const u32x4* tA = lds + sa * kTileU4;
+    const u32x4* tB = lds + sb * kTileU4;
 #pragma unroll
     for (int kk = 0; kk < kKK - 1; ++kk) {
-      kstep<A_MN, B_MN, kStepRead>(f, g, acc, st, fa, fb, kk + 1, la, lb, 0, nullptr, nullptr);
+      kstep<A_MN, B_MN, kStepRead>(f, g, acc, tA, tB, fa, fb, kk + 1, la, lb, 0, 0u, 0u);
       f = g;
     }
-    kstep<A_MN, B_MN, kStepLast>(f, g, acc, st, fa, fb, 0, la, lb, 0, nullptr, nullptr);
+    kstep<A_MN, B_MN, kStepLast>(f, g, acc, tA, tB, fa, fb, 0, la, lb, 0, 0u, 0u);
   }
-  // every load issued has landed and every wave is done with the stages
+  // every load issued has landed and every wave is done with the ring
   wait_vm(0);
   __syncthreads();
 }

@@ -425,12 +425,12 @@ struct ColsMN {
   const char* base;
   uint32_t off[kDma];
   size_t kstride;  // bytes per k-block
-  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
-    dma16(base + kt * kstride, off[i], tile, dma_slot0(i));
+  __device__ __forceinline__ void one(int i, int kt, uint32_t m0w) const {
+    dma16(base + kt * kstride, off[i], m0w + 1024u * i);
   }
-  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+  __device__ __forceinline__ void dma(int kt, uint32_t m0w) const {
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
+    for (int i = 0; i < kDma; ++i) one(i, kt, m0w);
   }
 };
 
@@ -457,16 +457,16 @@ struct WRowsMN {
   const char* base;     // W + first column of the tile
   uint32_t col2[kDma];  // byte offset of piece i's column
   int H, S, S_pad, c_lo, V;
-  __device__ __forceinline__ void one(int i, int kt, u32x4* tile) const {
+  __device__ __forceinline__ void one(int i, int kt, uint32_t m0w) const {
     const int kg = kt * kBK;
     const int sc = kg / S_pad;
     const int r0 = min((c_lo + sc) * S + (kg - sc * S_pad), V - 1);
     const int r = min((c_lo + sc) * S + (kg - sc * S_pad) + dma_mn_krow(i), V - 1);
-    dma16(base + (size_t)r0 * (2 * H), (uint32_t)((r - r0) * (2 * H)) + col2[i], tile, dma_slot0(i));
+    dma16(base + (size_t)r0 * (2 * H), (uint32_t)((r - r0) * (2 * H)) + col2[i], m0w + 1024u * i);
   }
-  __device__ __forceinline__ void dma(int kt, u32x4* tile) const {
+  __device__ __forceinline__ void dma(int kt, uint32_t m0w) const {
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) one(i, kt, tile);
+    for (int i = 0; i < kDma; ++i) one(i, kt, m0w);
   }
 };
 
