@@ -70,6 +70,74 @@ def traffic_for(kernel, digest):
     return rec.get("bytes_per_launch")
 
 
+# Calibration of the HBM byte counters: a plain device copy of a known size
+# (read COPY_BYTES, write COPY_BYTES per launch) run in the same process.
+COPY_BYTES = 1 << 30
+COPY_LAUNCHES = 4
+
+
+def copy_calibration(dev):
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_LAUNCHES):
+        torch.neg(src, out=dst)  # elementwise: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+
+
+def _counter_means(csv_dir, counter):
+    """Mean of `counter` per dispatch for each kernel (short name) in the
+    rocprofv3 counter-collection CSVs under csv_dir."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].split("<")[0].split("::")[-1]
+                key = (name, r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+def traffic_from(run_dir, command):
+    """Writes profiles/traffic_<kernel>.json for the GEMM kernels from two
+    counter runs of `bench.py --steps 2 --warmup 1 --no-cpu-baseline
+    --copy-calibration` (run_dir/fetch: --pmc FETCH_SIZE, run_dir/write:
+    --pmc WRITE_SIZE; both in KiB per dispatch).  Each counter is scaled by
+    what it reads for the calibration copy (COPY_BYTES each way)."""
+    fetch = _counter_means(os.path.join(run_dir, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(run_dir, "write"), "WRITE_SIZE")
+    copy = [k for k in fetch if "elementwise" in k or "neg" in k.lower()]
+    if not copy:
+        raise SystemExit(f"no calibration copy kernel among {sorted(fetch)}")
+    ck = copy[0]
+    f_scale = COPY_BYTES / (fetch[ck][0] * 1024.0)
+    w_scale = COPY_BYTES / (write[ck][0] * 1024.0)
+    digest = source_digest()
+    rows = []
+    for k in GEMM_KERNELS:
+        if k not in fetch or k not in write:
+            continue
+        fb = fetch[k][0] * 1024.0 * f_scale
+        wb = write[k][0] * 1024.0 * w_scale
+        rec = {"kernel": k, "source_digest": digest, "bytes_per_launch": fb + wb, "fetch_bytes": fb,
+               "write_bytes": wb, "dispatches": fetch[k][1], "calibration_kernel": ck,
+               "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{k}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        rows.append(rec)
+        print(f"{k}: fetch {fb / 1e9:.3f} GB, write {wb / 1e9:.3f} GB per launch", flush=True)
+    print(f"calibration {ck}: fetch scale {f_scale:.4f}, write scale {w_scale:.4f}", flush=True)
+    return rows
+
+
 def cpu_baseline(inp, rows, backward):
     import numpy as np
     import oracle
@@ -105,7 +173,15 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_fwd_bwd", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run plain copies of a known size (HBM counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter runs under DIR into profiles/traffic_*.json")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.traffic_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -159,6 +235,8 @@ def main():
     t1 = time.perf_counter()
     kern = rlk.profile_end()
     peak_reserved = torch.cuda.max_memory_reserved()
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     ms_wall = (t1 - t0) * 1e3 / args.steps
     ms_ev = ev0.elapsed_time(ev1) / args.steps
