@@ -41,11 +41,23 @@ WORKLOADS = {
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
 }
 
+# Dense-product workloads (rlk_gemm_bf16_nt): name -> (M, N, K, description).
+GEMM_WORKLOADS = {
+    "gemm_lm_head": (3482, 151936, 4096,
+                     "deterministic bf16 GEMM x W^T, the Qwen3-8B-shaped LM head at its 3482 active rows "
+                     "(M=3482, N=151936, K=4096), fp32 out"),
+    "gemm_8192": (8192, 8192, 8192, "deterministic bf16 GEMM, M=N=K=8192, fp32 out"),
+    "gemm_lm_head_bf16": (3482, 151936, 4096,
+                          "deterministic bf16 GEMM x W^T, the Qwen3-8B-shaped LM head at its 3482 active rows "
+                          "(M=3482, N=151936, K=4096), bf16 out"),
+    "gemm_8192_bf16": (8192, 8192, 8192, "deterministic bf16 GEMM, M=N=K=8192, bf16 out"),
+}
+
 # Kernels that carry the operator's MFMA work, with their algorithmic FLOPs
 # per step in units of 2*T_act*H*V (one contraction over the active rows):
 # forward logits; backward recompute; grad_h and grad_W (one launch), spread
 # over the kernel's launches in that step.
-GEMM_KERNELS = {"fwd_tiles": 1, "dz_tiles": 1, "grad_tiles": 2}
+GEMM_KERNELS = {"fwd_tiles": 1, "dz_tiles": 1, "grad_tiles": 2, "gemm_tiles": 1}
 
 
 def source_digest():
@@ -138,6 +150,75 @@ def traffic_from(run_dir, command):
     return rows
 
 
+def gemm_bench(args):
+    """Times rlk_gemm_bf16_nt on resident synthetic operands (A ~ N(0,1),
+    B ~ N(0, 1/sqrt(K))), with the vendor library's bf16 GEMM (torch.matmul,
+    hipBLASLt) on the same operands timed after it as context."""
+    import numpy as np
+    import torch
+
+    import selected_token_lm_amd as rlk
+    import synth
+
+    M, N, K, desc = GEMM_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    A_bits = synth.normal_bf16(synth.SEED_H, M, K)
+    B_bits = synth.normal_bf16(synth.SEED_W, N, K, float(1.0 / np.sqrt(K)))
+    A = torch.from_numpy(A_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    B = torch.from_numpy(B_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    flops = 2.0 * M * N * K
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / steps
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    rlk.profile_begin()
+    out_dtype = torch.bfloat16 if args.workload.endswith("_bf16") else torch.float32
+    ms = timed(lambda: rlk.gemm_bf16_nt(A, B, out_dtype=out_dtype), args.steps, args.warmup)
+    kern = rlk.profile_end()
+    n, tot = kern["gemm_tiles"]
+    k_ms = tot / n
+    Bt = B.t()
+    vendor_ms = timed(lambda: torch.matmul(A, Bt), args.steps, args.warmup)
+    achieved = flops / (k_ms * 1e-3)
+    out = {
+        "metric": "deterministic bf16 GEMM TFLOP/s (rlk_gemm_bf16_nt)",
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "kernel": "gemm_tiles", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
+                     "traffic": traffic_for("gemm_tiles", source_digest()), "flops_per_launch": flops,
+                     "avg_launch_ms": k_ms},
+        "context": {"vendor_bf16_gemm": "torch.matmul (hipBLASLt), same operands, not deterministic by contract",
+                    "vendor_ms": vendor_ms, "vendor_tflops": flops / (vendor_ms * 1e-3) / 1e12},
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, rows, backward):
     import numpy as np
     import oracle
@@ -170,7 +251,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_8b_fwd_bwd", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="qwen3_8b_fwd_bwd", choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,6 +274,10 @@ def main():
 
     import selected_token_lm_amd as rlk
     import synth
+
+    if args.workload in GEMM_WORKLOADS:
+        gemm_bench(args)
+        return
 
     T, H, V, mask, do_bwd, desc = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -168,6 +168,30 @@ rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts,
                          const int32_t* y, int64_t T, int32_t ignore_index,
                          float* logp, float* lse, void* stream);
 
+/* Output element types of rlk_gemm_bf16_nt. */
+enum { RLK_DT_F32 = 0, RLK_DT_BF16 = 1 };
+
+/* Deterministic, batch-invariant dense product ("vLLM RL-Kernel v0.1.0:
+ * Bitwise Train-Rollout Consistency on ROCm", section "Implementation on
+ * ROCm": deterministic MFMA-based GEMM kernels; section "Boundary Fixes in
+ * the RL-Kernel Strict Path": for GEMM, the K-dimension reduction,
+ * accumulation precision, epilogue and materialization boundary are fixed):
+ *     C[i, j] = sum_k A[i, k] * B[j, k]
+ *   A  bf16 [M, K]      row-major (K contiguous), e.g. activations x
+ *   B  bf16 [N, K]      row-major (K contiguous), e.g. a weight W for x W^T
+ *   C  [M, ldc] out     fp32 (c_dtype RLK_DT_F32) or bf16 (RLK_DT_BF16:
+ *                       the fp32 result rounded once to nearest even);
+ *                       columns N .. ldc-1 are not written
+ * Contract: one fp32 v_mfma_f32_32x32x16_bf16 accumulation chain per
+ * element, k ascending in steps of 16, no split-K -- the chain of the
+ * logits above.  Hence C[i, :] depends only on A[i, :] and B (bitwise
+ * invariant to M, to the other rows of A and to their order), and repeated
+ * runs are bit-identical.
+ * Requires 0 < K <= 2^20 with K % 64 == 0, 0 <= M, N <= 2^24, ldc >= N with
+ * ldc % 4 == 0; M == 0 or N == 0 returns RLK_OK without launching. */
+rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                            void* C, int64_t ldc, int32_t c_dtype, void* stream);
+
 /* Per-kernel timing for benchmarks; computes nothing.  After
  * rlk_profile_begin(), every kernel the library launches (on any stream) is
  * bracketed by two HIP events recorded on that stream.  rlk_profile_end()

@@ -11,6 +11,7 @@ library is missing or the device is not gfx950, calls raise.
     grad_h, grad_W = linear_logp_bwd(h, W, y, lse, g)
     part = lse_partial(h, W_shard, y, vocab_start, V_global)   # [T, 4] records
     logp, lse = lse_merge(torch.stack(parts), y)
+    C = gemm_bf16_nt(A, B)                  # deterministic A @ B^T
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ import torch
 __all__ = [
     "IGNORE_INDEX", "RlkError", "lib", "library_path", "contract_version",
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
-    "lse_merge", "linear_logp", "profile_begin", "profile_end",
+    "lse_merge", "linear_logp", "gemm_bf16_nt", "profile_begin", "profile_end",
 ]
 
 IGNORE_INDEX = -100
@@ -50,6 +51,8 @@ _SIGNATURES = {
                                _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
     "rlk_lse_merge": (_i32, [_c_void_p, _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p,
                              _c_void_p]),
+    "rlk_gemm_bf16_nt": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _i32,
+                                _c_void_p]),
     "rlk_profile_begin": (_i32, []),
     "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
 }
@@ -198,6 +201,30 @@ def lse_merge(parts, y, ignore_index: int = IGNORE_INDEX):
                                _stream()),
            "rlk_lse_merge")
     return logp, lse
+
+
+def gemm_bf16_nt(A, B, out_dtype=torch.float32):
+    """Deterministic, batch-invariant A @ B^T for bf16 A [M, K] and B [N, K].
+
+    out_dtype torch.float32 or torch.bfloat16 (rounded once).  K % 64 == 0.
+    """
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A must be [M, K] and B [N, K]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    A, B = A.contiguous(), B.contiguous()
+    M, K = A.shape
+    N = B.shape[0]
+    ldc = (N + 3) // 4 * 4
+    C = torch.empty((M, ldc), dtype=out_dtype, device=A.device)
+    _check(lib().rlk_gemm_bf16_nt(_ptr(A), _ptr(B), M, N, K, _ptr(C), ldc,
+                                  0 if out_dtype == torch.float32 else 1, _stream()),
+           "rlk_gemm_bf16_nt")
+    return C[:, :N] if ldc != N else C
 
 
 def profile_begin():

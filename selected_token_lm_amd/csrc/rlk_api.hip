@@ -43,6 +43,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 constexpr int64_t kMaxT = int64_t(1) << 24;
 constexpr int64_t kMaxH = 1 << 16;
 constexpr int64_t kMaxV = 8000000;  // 32 splits x chunks stay within one grid dimension
+constexpr int64_t kMaxGemmMN = int64_t(1) << 24;
+constexpr int64_t kMaxGemmK = int64_t(1) << 20;  // 255 rows x K x 2 bytes stay below 2^32
 
 struct Geom {
   int64_t V, S, cps, S_pad;
@@ -488,6 +490,35 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
               : (last ? rlk::grad_tiles<false, true> : rlk::grad_tiles<false, false>);
     RLK_LAUNCH_FN("grad_tiles", kfn, dim3((unsigned)(gh_blocks + gw_blocks)), dim3(rlk::kThreads), st, ha, wa);
   }
+  return ok();
+}
+
+rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                            int32_t c_dtype, void* stream) {
+  if (M < 0 || N < 0 || M > kMaxGemmMN || N > kMaxGemmMN)
+    return fail(RLK_ERR_BAD_SHAPE, "M=%lld N=%lld out of [0, 2^24]", (long long)M, (long long)N);
+  if (K <= 0 || K % 64 != 0 || K > kMaxGemmK)
+    return fail(RLK_ERR_BAD_SHAPE, "K=%lld must be a positive multiple of 64 up to 2^20", (long long)K);
+  if (c_dtype != RLK_DT_F32 && c_dtype != RLK_DT_BF16) return fail(RLK_ERR_BAD_ARG, "c_dtype=%d", c_dtype);
+  if (M == 0 || N == 0) return ok();
+  if (ldc < N || ldc % 4 != 0) return fail(RLK_ERR_BAD_SHAPE, "ldc=%lld must be >= N and a multiple of 4", (long long)ldc);
+  if (!A || !B || !C) return fail(RLK_ERR_NULL_ARG, "A, B and C are required");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return fail(RLK_ERR_BAD_ALIGNMENT, "A, B, C must be 16-byte aligned");
+  RLK_TRY(check_device());
+  rlk::GemmArgs ga;
+  ga.A = static_cast<const uint16_t*>(A);
+  ga.B = static_cast<const uint16_t*>(B);
+  ga.M = (int)M;
+  ga.N = (int)N;
+  ga.K = (int)K;
+  ga.rtiles = (int)ceil_div(M, rlk::kBM);
+  ga.ctiles = (int)ceil_div(N, rlk::kBN);
+  ga.ldc = ldc;
+  ga.c_bf16 = c_dtype == RLK_DT_BF16;
+  ga.C = C;
+  const int64_t blocks = 8 * ceil_div((int64_t)ga.rtiles * ga.ctiles, 8);
+  RLK_TRY(check_grid(blocks));
+  RLK_LAUNCH(gemm_tiles, dim3((unsigned)blocks), dim3(rlk::kThreads), static_cast<hipStream_t>(stream), ga);
   return ok();
 }
 

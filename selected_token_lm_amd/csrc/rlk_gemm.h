@@ -434,17 +434,19 @@ __device__ __forceinline__ int xcd_tile(int live, int bid) {
 }
 
 // Tile id -> (fast index f < F, slow index c < C) in groups of GM fast
-// indices: consecutive ids walk GM values of f, then the next c, so the
-// ~32 tiles in flight on one XCD form a GM x (32 / GM) block of the output
-// and share their operand rows in L2.
-constexpr int kGroupM = 4;
-__device__ __forceinline__ void grouped_tile(int id, int F, int& f, int& c, int C) {
-  const int per_group = kGroupM * C;
+// indices: consecutive ids walk the GM values of f of a group, then the
+// next c.  With GM = min(8, F) the ~32 tiles an XCD runs together (its
+// contiguous id range, see xcd_tile) form an 8 x 4 block whose 12 operand
+// tiles per k-block are shared in its L2 (measured best among group sizes
+// 4..16, on the LM-head and on square products).
+__device__ __forceinline__ int row_group(int F) { return min(8, F); }
+__device__ __forceinline__ void grouped_tile(int id, int F, int& f, int& c, int C, int GM) {
+  const int per_group = GM * C;
   const int grp = id / per_group;
-  const int gm = min(kGroupM, F - grp * kGroupM);
+  const int gm = min(GM, F - grp * GM);
   const int within = id - grp * per_group;
   c = within / gm;
-  f = grp * kGroupM + (within - c * gm);
+  f = grp * GM + (within - c * gm);
 }
 
 }  // namespace rlk

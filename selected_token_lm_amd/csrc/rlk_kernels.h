@@ -11,6 +11,8 @@
 //                        grad_h: fp32 accumulator += dz W; bf16 after the last group
 //                        grad_W: rows of the group = dz^T h  (K = active rows)
 //   zero_rows          zero grad_h rows of inactive rows
+// Dense product (same engine):
+//   gemm_tiles         C = A B^T, one MFMA chain per element
 #pragma once
 
 #include "rlk_gemm.h"
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int id = xcd_tile(rtiles * C, blockIdx.x);
   if (id < 0) return;
   int rt, ct;
-  grouped_tile(id, rtiles, rt, ct, C);
+  grouped_tile(id, rtiles, rt, ct, C, row_group(rtiles));
   const int i0 = rt * kBM;
   const int sl = ct / a.tg.tps, j = ct - sl * a.tg.tps;
   const int sbeg = (a.gm.s0 + sl) * a.gm.S;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int id = xcd_tile(rtiles * C, blockIdx.x);
   if (id < 0) return;
   int rt, ct;
-  grouped_tile(id, rtiles, rt, ct, C);
+  grouped_tile(id, rtiles, rt, ct, C, row_group(rtiles));
   const int i0 = rt * kBM;
   const int sc = ct / a.tg.tps, j = ct - sc * a.tg.tps;
   const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
@@ -487,7 +489,7 @@ struct GradWArgs {
 // Both operands are MN mode.  Written once, fp32.  Tile id: (H tile, v tile).
 __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4* lds) {
   int nt, vt;
-  grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps);
+  grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps, row_group(a.n_tiles));
   const int sc = vt / a.tps, j = vt - sc * a.tps;
   const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));
@@ -540,7 +542,7 @@ struct GradHArgs {
 template <bool kFirst, bool kLast>
 __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int n_act, u32x4* lds) {
   int rt, nt;
-  grouped_tile(id, rtiles, rt, nt, a.n_tiles);
+  grouped_tile(id, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
   const int i0 = rt * kBM, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
   int dst[kMI];  // output rows of this lane's active rows, loaded ahead
@@ -626,6 +628,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nw = wa.grad_W ? wa.n_tiles * wa.bg.G * wa.tps : 0;
   const int id = xcd_tile(nw, bid - nh_blocks);
   if (id >= 0) gradw_tile(wa, id, n_act, lds);
+}
+
+
+// ---------------------------------------------------------------------------
+// Deterministic dense product C = A B^T on the same tile engine: every
+// element is one MFMA chain over k ascending, whatever the tile it falls in,
+// so a row of C depends only on its row of A (and B).  Tile id: (row tile of
+// A, row tile of B).  Rows past M / N are clamped loads that are never
+// stored.  c_bf16: store bf16 (round to nearest even, once) instead of fp32.
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+  const uint16_t* A;  // [M, K]
+  const uint16_t* B;  // [N, K]
+  int M, N, K;
+  int rtiles, ctiles;
+  int64_t ldc;
+  int c_bf16;
+  void* C;
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tiles(GemmArgs a) {
+  __shared__ u32x4 lds[kLdsU4];
+  const int id = xcd_tile(a.rtiles * a.ctiles, blockIdx.x);
+  if (id < 0) return;
+  int rt, ct;
+  grouped_tile(id, a.rtiles, rt, ct, a.ctiles, row_group(a.rtiles));
+  const int m0 = rt * kBM, n0 = ct * kBN;
+  const RowsK LA = rows_k(a.A + (size_t)m0 * a.K, min(kBM, a.M - m0) - 1, a.K);
+  const RowsK LB = rows_k(a.B + (size_t)n0 * a.K, min(kBN, a.N - n0) - 1, a.K);
+  Acc acc;
+  acc_zero(acc);
+  gemm256<false, false>(LA, LB, a.K / kBK, acc, lds);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi) {
+    const int i = m0 + acc_row(wm, mi, lane);
+    if (i >= a.M) continue;
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = n0 + acc_col4(wn, ni, q, lane);
+        const f32x16& c = acc.c[mi][ni];
+        const float v0 = c[4 * q], v1 = c[4 * q + 1], v2 = c[4 * q + 2], v3 = c[4 * q + 3];
+        if (a.c_bf16) {
+          uint16_t* row = static_cast<uint16_t*>(a.C) + (size_t)i * a.ldc;
+          const uint32_t p01 = pack_bf16x2(v0, v1), p23 = pack_bf16x2(v2, v3);
+          if (j + 3 < a.N) {
+            *reinterpret_cast<uint2*>(row + j) = make_uint2(p01, p23);
+          } else {
+            if (j < a.N) row[j] = (uint16_t)(p01 & 0xFFFFu);
+            if (j + 1 < a.N) row[j + 1] = (uint16_t)(p01 >> 16);
+            if (j + 2 < a.N) row[j + 2] = (uint16_t)(p23 & 0xFFFFu);
+          }
+        } else {
+          float* row = static_cast<float*>(a.C) + (size_t)i * a.ldc;
+          if (j + 3 < a.N) {
+            *reinterpret_cast<float4*>(row + j) = make_float4(v0, v1, v2, v3);
+          } else {
+            if (j < a.N) row[j] = v0;
+            if (j + 1 < a.N) row[j + 1] = v1;
+            if (j + 2 < a.N) row[j + 2] = v2;
+          }
+        }
+      }
+  }
 }
 
 

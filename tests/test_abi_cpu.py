@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(rlk.library_path)
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -135,6 +135,30 @@ def test_merge_validation():
     assert L.rlk_lse_merge(FAKE, 2, FAKE, -1, -100, FAKE, FAKE, None) == BAD_SHAPE
     assert L.rlk_lse_merge(MISALIGNED, 2, FAKE, 8, -100, FAKE, FAKE, None) == BAD_ALIGN
     assert L.rlk_lse_merge(FAKE, 2, FAKE, 0, -100, FAKE, FAKE, None) == OK
+
+
+def gemm(A=FAKE, B=FAKE, M=300, N=260, K=128, C=FAKE, ldc=260, dt=0):
+    return rlk.lib().rlk_gemm_bf16_nt(A, B, M, N, K, C, ldc, dt, None)
+
+
+def test_gemm_validation():
+    assert gemm(A=None) == NULL_ARG
+    assert gemm(B=None) == NULL_ARG
+    assert gemm(C=None) == NULL_ARG
+    assert gemm(K=0) == BAD_SHAPE
+    assert gemm(K=96) == BAD_SHAPE
+    assert gemm(K=1 << 21) == BAD_SHAPE
+    assert gemm(M=-1) == BAD_SHAPE
+    assert gemm(N=(1 << 24) + 1) == BAD_SHAPE
+    assert gemm(ldc=259) == BAD_SHAPE
+    assert gemm(ldc=262) == BAD_SHAPE
+    assert gemm(dt=2) == BAD_ARG
+    assert gemm(A=MISALIGNED) == BAD_ALIGN
+    assert gemm(C=MISALIGNED) == BAD_ALIGN
+    # empty products launch nothing; their pointers may be NULL
+    assert gemm(M=0, A=None, C=None) == OK
+    assert gemm(N=0, B=None, C=None) == OK
+    assert gemm(M=0, K=96) == BAD_SHAPE
 
 
 def test_binding_refuses_host_tensors():
