@@ -37,6 +37,9 @@ WORKLOADS = {
                          "linear_logp fwd+bwd, Qwen3-8B-shaped LM head (T=4096, H=4096, V=151936, 15% rows ignored)"),
     "qwen3_8b_fwd": (4096, 4096, 151936, 0.15, False,
                      "linear_logp fwd, Qwen3-8B-shaped LM head (T=4096, H=4096, V=151936, 15% rows ignored)"),
+    "qwen3_8b_fwd_bwd_saved": (4096, 4096, 151936, 0.15, True,
+                               "linear_logp fwd+bwd, save-logits variant (fp32 logits kept between the passes, "
+                               "no recompute), Qwen3-8B-shaped LM head (T=4096, H=4096, V=151936, 15% rows ignored)"),
     "qwen3_30b_a3b_fwd_bwd": (16384, 2048, 151936, 0.15, True,
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
 }
@@ -294,7 +297,14 @@ def main():
     torch.cuda.synchronize()
     reserved0 = torch.cuda.memory_reserved()
 
+    saved = args.workload.endswith("_saved")
+    zsave = torch.empty((T, rlk.saved_logits_ld(V)), dtype=torch.float32, device=dev) if saved else None
+
     def step():
+        if saved:
+            logp, lse, _ = rlk.linear_logp_fwd_save(h, W, y, ws=ws_f, zsave=zsave)
+            rlk.linear_logp_bwd_saved(h, W, y, lse, g, zsave, ws=ws_b)
+            return
         logp, lse = rlk.linear_logp_fwd(h, W, y, ws=ws_f)
         if do_bwd:
             rlk.linear_logp_bwd(h, W, y, lse, g, ws=ws_b)
@@ -326,7 +336,9 @@ def main():
     ms_wall = (t1 - t0) * 1e3 / args.steps
     ms_ev = ev0.elapsed_time(ev1) / args.steps
     ms = max(ms_wall, ms_ev)
-    flops_step = 2.0 * T_act * H * V * (4 if do_bwd else 1)
+    # algorithmic contractions per step: forward, recompute (not in the
+    # save-logits variant), grad_W, grad_h
+    flops_step = 2.0 * T_act * H * V * ((3 if saved else 4) if do_bwd else 1)
 
     digest = source_digest()
     kernels = {}
@@ -372,7 +384,8 @@ def main():
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "roofline": roofline,
         "kernels": kernels,
-        "workspace_bytes": int(ws_f.numel() + (ws_b.numel() if do_bwd else 0)),
+        "workspace_bytes": int(ws_f.numel() + (ws_b.numel() if do_bwd else 0)
+                               + (zsave.numel() * 4 if saved else 0)),
         "peak_reserved_delta_mb": (peak_reserved - reserved0) / 2**20,
         "source_digest": digest,
     }

@@ -138,6 +138,39 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y,
                                void* grad_h, float* grad_W,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* Save-logits variant of the forward and backward: the pages' published
+ * fast path ("Announcing RL-Kernel for vime", section "Validation and
+ * Benchmarks": FusedLinearLogpSM90Op in the save-logits fused-tile
+ * full-gradient path; section "Why the Fused Path Wins", fourth reason: a
+ * controlled workspace traded for backward speed).  The forward also stores
+ * the fp32 logits of the active rows into the caller's buffer `zsave`; the
+ * backward then forms dz from them instead of recomputing the logit tiles
+ * (6 instead of 8 H x V multiply-adds per active token).  The saved logits
+ * are the same fp32 values the chunk statistics are taken from, so logp,
+ * lse, grad_h and grad_W are bit-identical to rlk_linear_logp_fwd /
+ * rlk_linear_logp_bwd.  This materialises a [T, V]-sized fp32 buffer; the
+ * default path above never does.
+ *   zsave  fp32, row t (original row index) of the logits at zsave + t*ldzs,
+ *          split s (of the 32) at column s * S_pad, S_pad = ceil(S/64)*64,
+ *          S = ceil(V/32); columns past a split's width and rows of
+ *          inactive targets are not written
+ *   ldzs   row stride in floats: a multiple of 4, >= rlk_saved_logits_ld(V)
+ * The forward's logp, lse and workspace are those of rlk_linear_logp_fwd
+ * (lse is required here); the backward takes the workspace of
+ * rlk_linear_logp_bwd and zsave must hold the forward's output for the same
+ * h, W and y. */
+int64_t rlk_saved_logits_ld(int64_t V); /* 32 * S_pad; 0 for invalid V */
+rlk_status rlk_linear_logp_fwd_save(const void* h, const void* W, const int32_t* y,
+                                    int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                                    float* logp, float* lse, float* zsave, int64_t ldzs,
+                                    void* ws, size_t ws_bytes, void* stream);
+rlk_status rlk_linear_logp_bwd_saved(const void* h, const void* W, const int32_t* y,
+                                     const float* lse, const float* g,
+                                     const float* zsave, int64_t ldzs,
+                                     int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                                     void* grad_h, float* grad_W,
+                                     void* ws, size_t ws_bytes, void* stream);
+
 /* Statistics of one vocabulary range [vocab_start, vocab_start + vocab_len)
  * of a vocabulary of V_global rows, as one tensor-parallel rank would hold it
  * ("Why the Fused Path Wins", third reason; "vLLM RL-Kernel v0.1.0 ...",

@@ -12,6 +12,8 @@ library is missing or the device is not gfx950, calls raise.
     part = lse_partial(h, W_shard, y, vocab_start, V_global)   # [T, 4] records
     logp, lse = lse_merge(torch.stack(parts), y)
     C = gemm_bf16_nt(A, B)                  # deterministic A @ B^T
+    logp, lse, z = linear_logp_fwd_save(h, W, y)          # save-logits variant
+    grad_h, grad_W = linear_logp_bwd_saved(h, W, y, lse, g, z)
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ import torch
 __all__ = [
     "IGNORE_INDEX", "RlkError", "lib", "library_path", "contract_version",
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
-    "lse_merge", "linear_logp", "gemm_bf16_nt", "profile_begin", "profile_end",
+    "lse_merge", "linear_logp", "gemm_bf16_nt", "linear_logp_fwd_save", "linear_logp_bwd_saved",
+    "saved_logits_ld", "profile_begin", "profile_end",
 ]
 
 IGNORE_INDEX = -100
@@ -53,6 +56,13 @@ _SIGNATURES = {
                              _c_void_p]),
     "rlk_gemm_bf16_nt": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _i32,
                                 _c_void_p]),
+    "rlk_saved_logits_ld": (_i64, [_i64]),
+    "rlk_linear_logp_fwd_save": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                                        _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _size,
+                                        _c_void_p]),
+    "rlk_linear_logp_bwd_saved": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _i64, _i64, _i64, _i64, _i32, _c_void_p,
+                                         _c_void_p, _c_void_p, _size, _c_void_p]),
     "rlk_profile_begin": (_i32, []),
     "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
 }
@@ -164,6 +174,59 @@ def linear_logp_bwd(h, W, y, lse, g, ignore_index: int = IGNORE_INDEX,
                                      ignore_index, _ptr(grad_h), _ptr(grad_W), _ptr(ws), n,
                                      _stream()),
            "rlk_linear_logp_bwd")
+    return grad_h, grad_W
+
+
+def saved_logits_ld(V: int) -> int:
+    """Row stride (floats) of the saved-logits buffer for a vocabulary of V rows."""
+    return int(lib().rlk_saved_logits_ld(V))
+
+
+def linear_logp_fwd_save(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None, zsave=None):
+    """Forward that also keeps the fp32 logits of the active rows.
+
+    Returns (logp, lse, zsave) with zsave fp32 [T, saved_logits_ld(V)] in the
+    split layout of include/rlk.h; logp and lse equal linear_logp_fwd's bits.
+    """
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    ld = saved_logits_ld(V)
+    logp = torch.empty(T, dtype=torch.float32, device=h.device)
+    lse = torch.empty(T, dtype=torch.float32, device=h.device)
+    if zsave is None:
+        zsave = torch.empty((T, ld), dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws, n = _workspace(OP_FWD, T, H, V, h.device)
+    else:
+        n = ws.numel()
+    _check(lib().rlk_linear_logp_fwd_save(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
+                                          _ptr(logp), _ptr(lse), _ptr(zsave), zsave.stride(0),
+                                          _ptr(ws), n, _stream()),
+           "rlk_linear_logp_fwd_save")
+    return logp, lse, zsave
+
+
+def linear_logp_bwd_saved(h, W, y, lse, g, zsave, ignore_index: int = IGNORE_INDEX,
+                          need_grad_h: bool = True, need_grad_W: bool = True, ws=None):
+    """linear_logp_bwd from the logits saved by linear_logp_fwd_save (no recompute)."""
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    lse = lse.to(torch.float32).contiguous()
+    g = g.to(torch.float32).contiguous()
+    if zsave.dtype != torch.float32 or zsave.dim() != 2 or zsave.stride(1) != 1:
+        raise ValueError("zsave must be the float32 [T, ld] buffer of linear_logp_fwd_save")
+    grad_h = torch.empty((T, H), dtype=torch.bfloat16, device=h.device) if need_grad_h else None
+    grad_W = torch.empty((V, H), dtype=torch.float32, device=h.device) if need_grad_W else None
+    if ws is None:
+        ws, n = _workspace(OP_BWD, T, H, V, h.device)
+    else:
+        n = ws.numel()
+    _check(lib().rlk_linear_logp_bwd_saved(_ptr(h), _ptr(W), _ptr(y), _ptr(lse), _ptr(g), _ptr(zsave),
+                                           zsave.stride(0), T, H, V, ignore_index, _ptr(grad_h),
+                                           _ptr(grad_W), _ptr(ws), n, _stream()),
+           "rlk_linear_logp_bwd_saved")
     return grad_h, grad_W
 
 

@@ -266,7 +266,8 @@ rlk_status split_range(int64_t vocab_start, int64_t vocab_len, int64_t V_global,
 // Shared forward body: statistics of splits [s0, s0+n) then the epilogue.
 rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V_global,
                        int32_t ignore_index, int s0, int nsplit, int64_t vocab_start, int64_t vocab_len, int mode,
-                       float* logp, float* lse, rlk_lse_partial_t* pout, void* ws, hipStream_t st) {
+                       float* logp, float* lse, rlk_lse_partial_t* pout, void* ws, hipStream_t st,
+                       float* zsave = nullptr, int64_t ldzs = 0) {
   const Geom g = geom_of(V_global);
   const FwdWs L = fwd_layout(T, H, V_global);
   char* base = static_cast<char*>(ws);
@@ -305,7 +306,13 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   // grid: every row tile of T (the kernel keeps those of active rows)
   const int64_t fwd_blocks = 8 * ceil_div(ceil_div(T, rlk::kBM) * nsplit * fa.tg.tps, 8);
   RLK_TRY(check_grid(fwd_blocks));
-  RLK_LAUNCH(fwd_tiles, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
+  fa.zsave = zsave;
+  fa.ldzs = ldzs;
+  fa.zs_spad = (int)ceil_div(g.S, 64) * 64;
+  if (zsave)
+    RLK_LAUNCH_FN("fwd_tiles", rlk::fwd_tiles<true>, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
+  else
+    RLK_LAUNCH_FN("fwd_tiles", rlk::fwd_tiles<false>, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
 
   RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
              nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
@@ -393,9 +400,15 @@ rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts, const 
   return ok();
 }
 
-rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, const float* lse, const float* g,
-                               int64_t T, int64_t H, int64_t V, int32_t ignore_index, void* grad_h, float* grad_W,
-                               void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared backward body: dz per group of splits (recomputed tiles, or from
+// the forward's saved logits when zsave != NULL), then grad_h / grad_W.
+rlk_status run_backward(const void* h, const void* W, const int32_t* y, const float* lse, const float* g,
+                        const float* zsave, int64_t ldzs, int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                        void* grad_h, float* grad_W, void* ws, size_t ws_bytes, void* stream) {
   RLK_TRY(check_common(h, W, y, T, H, V));
   if (T == 0) return ok();
   if (!lse || !g || !ws) return fail(RLK_ERR_NULL_ARG, "lse, g and ws are required");
@@ -461,7 +474,11 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
     da.tg.tps = tps;
     da.bg = bg;
     da.dZ = dZ;
-    RLK_LAUNCH(dz_tiles, dim3((unsigned)dz_blocks), dim3(rlk::kThreads), st, da);
+    if (zsave)
+      RLK_LAUNCH(dz_saved, dim3((unsigned)ceil_div(bg.ldz / 8, 256), (unsigned)L.T_pad), dim3(256), st, zsave, ldzs,
+                 idx, rowinfo, n_act, gm, bg, dZ);
+    else
+      RLK_LAUNCH(dz_tiles, dim3((unsigned)dz_blocks), dim3(rlk::kThreads), st, da);
 
     rlk::GradWArgs wa;
     wa.dZ = dZ;
@@ -491,6 +508,54 @@ rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, c
     RLK_LAUNCH_FN("grad_tiles", kfn, dim3((unsigned)(gh_blocks + gw_blocks)), dim3(rlk::kThreads), st, ha, wa);
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y, const float* lse, const float* g,
+                               int64_t T, int64_t H, int64_t V, int32_t ignore_index, void* grad_h, float* grad_W,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return run_backward(h, W, y, lse, g, nullptr, 0, T, H, V, ignore_index, grad_h, grad_W, ws, ws_bytes, stream);
+}
+
+int64_t rlk_saved_logits_ld(int64_t V) {
+  if (V <= 0 || V > kMaxV) return 0;
+  return rlk::kNSplit * ceil_div(geom_of(V).S, 64) * 64;
+}
+
+rlk_status rlk_linear_logp_fwd_save(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V,
+                                    int32_t ignore_index, float* logp, float* lse, float* zsave, int64_t ldzs,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  RLK_TRY(check_common(h, W, y, T, H, V));
+  if (T == 0) return ok();
+  if (!logp || !lse || !zsave || !ws) return fail(RLK_ERR_NULL_ARG, "logp, lse, zsave and ws are required");
+  if (!aligned16(logp) || !aligned16(lse) || !aligned16(zsave) || !aligned16(ws))
+    return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse, zsave, ws must be 16-byte aligned");
+  if (ldzs < rlk_saved_logits_ld(V) || ldzs % 4 != 0)
+    return fail(RLK_ERR_BAD_SHAPE, "ldzs=%lld must be a multiple of 4 and >= %lld", (long long)ldzs,
+                (long long)rlk_saved_logits_ld(V));
+  if (ws_bytes < fwd_layout(T, H, V).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, H, V).total, ws_bytes);
+  RLK_TRY(check_device());
+  RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
+                      static_cast<hipStream_t>(stream), zsave, ldzs));
+  return ok();
+}
+
+rlk_status rlk_linear_logp_bwd_saved(const void* h, const void* W, const int32_t* y, const float* lse, const float* g,
+                                     const float* zsave, int64_t ldzs, int64_t T, int64_t H, int64_t V,
+                                     int32_t ignore_index, void* grad_h, float* grad_W, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (T > 0) {
+    if (!zsave) return fail(RLK_ERR_NULL_ARG, "zsave is required");
+    if (!aligned16(zsave)) return fail(RLK_ERR_BAD_ALIGNMENT, "zsave must be 16-byte aligned");
+    if (ldzs < rlk_saved_logits_ld(V) || ldzs % 4 != 0)
+      return fail(RLK_ERR_BAD_SHAPE, "ldzs=%lld must be a multiple of 4 and >= %lld", (long long)ldzs,
+                  (long long)rlk_saved_logits_ld(V));
+  }
+  return run_backward(h, W, y, lse, g, zsave, ldzs, T, H, V, ignore_index, grad_h, grad_W, ws, ws_bytes, stream);
 }
 
 rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,

@@ -7,6 +7,7 @@
 //   merge_parts        tree over per-range statistics (rlk_lse_merge)
 // Backward (per group of vocabulary splits, ascending):
 //   dz_tiles           recomputed logits -> dz = g (onehot - softmax), bf16
+//   dz_saved           the same dz from logits the forward saved (no recompute)
 //   grad_tiles         one launch of the group's tiles of
 //                        grad_h: fp32 accumulator += dz W; bf16 after the last group
 //                        grad_W: rows of the group = dz^T h  (K = active rows)
@@ -90,16 +91,14 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
   c1 = min(c0 + kChunk, send);
 }
 
-// Element k = 16 ni + r (ni = 0..3, r = 0..15) of one row block of the
-// accumulator, selected by a per-lane k (a chain of compares and selects;
-// indexing a register array with k would move the array to memory).
-__device__ __forceinline__ float pick64(const f32x16 (&c)[kNI], int k) {
-  float v = 0.f;
+// Element k of a row's 64 values, selected by a per-lane k (a chain of
+// compares and selects; indexing a register array with k would move the
+// array to memory).
+__device__ __forceinline__ float pick64(const float (&v)[64], int k) {
+  float x = 0.f;
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v = (k == 16 * ni + r) ? c[ni][r] : v;
-  return v;
+  for (int e = 0; e < 64; ++e) x = (k == e) ? v[e] : x;
+  return x;
 }
 
 // Balanced pairwise tree over e[0..63]: adjacent pairs, then pairs of pairs.
@@ -152,8 +151,15 @@ struct FwdArgs {
   size_t rec_stride;
   float2* rec;
   float* zt;
+  float* zsave;  // kSave: fp32 logits of active rows: row t, split s, column c of
+                 // the split at zsave + t * ldzs + s * zs_spad + c
+  int64_t ldzs;
+  int zs_spad;   // S rounded up to 64
 };
 
+// kSave: also store every active row's fp32 logits (the values the chunk
+// statistics are taken from) for a backward without recompute.
+template <bool kSave>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_tiles(FwdArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   // tiles: the active-row tiles x every 256-column tile of the range (the
@@ -178,6 +184,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   int tgt[kMI];
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) tgt[mi] = a.yA[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
+  int trow[kMI];  // original rows (kSave only)
+  if (kSave) {
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) trow[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
+  }
 
   const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
   const RowsK B = rows_k(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
@@ -194,30 +205,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
     const int i = i0 + acc_row(wm, mi, lane);
+    // the row's 64 values of this lane, out of the accumulator once
+    float v[64];
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[16 * ni + r] = acc.c[mi][ni][r];
+    if (kSave && i < n_act) {
+      // columns cc0 + 32 ni + 8 q + 4 hh + 0..3 (the chunk's first `width`);
+      // cc0 - sbeg is a multiple of 128, so every float4 is 16-byte aligned
+      float* zr = a.zsave + (size_t)trow[mi] * a.ldzs + (size_t)(a.gm.s0 + sl) * a.zs_spad + (cc0 - sbeg) + 4 * hh;
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 32 * ni + 8 * q;  // column of element 0, relative to cc0 + 4 hh
+          const float* e = v + 16 * ni + 4 * q;
+          if (c + 4 <= lim) {
+            *reinterpret_cast<float4*>(zr + c) = make_float4(e[0], e[1], e[2], e[3]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (c + u < lim) zr[c + u] = e[u];
+          }
+        }
+    }
+    // target logit: rare (a row's target lies in a given chunk about once in
+    // a thousand), so the select chain runs only when some lane needs it
     const int tc = tgt[mi] - cc0;
-    if (i < n_act && tc >= 0 && tc < width && ((tc >> 2) & 1) == hh)
-      a.zt[i] = pick64(acc.c[mi], ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3));
-    if (width < kChunk) {
+    const bool hit = i < n_act && tc >= 0 && tc < width && ((tc >> 2) & 1) == hh;
+    if (__builtin_amdgcn_ballot_w64(hit)) {
+      const float z = pick64(v, ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3));
+      if (hit) a.zt[i] = z;
+    }
+    if (width < kChunk) {  // short last chunk of a split (wave-uniform)
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) acc.c[mi][ni][r] = -INFINITY;
+          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) v[16 * ni + r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc.c[mi][ni][r]);
+    for (int k = 0; k < 64; ++k) mx = fmaxf(mx, v[k]);
     float lo, hi;
     lane_halves(mx, lo, hi);
     mx = fmaxf(lo, hi);
-    float e[64];
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[16 * ni + r] = rlk_exp(acc.c[mi][ni][r] - mx);
-    lane_halves(tree_sum64(e), lo, hi);
+    for (int k = 0; k < 64; ++k) v[k] = rlk_exp(v[k] - mx);
+    lane_halves(tree_sum64(v), lo, hi);
     if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = make_float2(mx, lo + hi);
   }
 }
@@ -417,6 +453,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
       }
   }
+}
+
+// dz of the group from saved logits (the forward's kSave output, same split
+// layout as dZ) instead of a recomputed tile: the same z bits, primitives
+// and rounding as dz_tiles, so the same dz bits.  One thread per 8
+// consecutive dZ columns of one compacted row; grid (G * S_pad / 8 / 256,
+// T_pad); rows past the active row tiles are left alone (never read).
+__global__ __launch_bounds__(256) void dz_saved(const float* __restrict__ zsave, int64_t ldzs,
+                                                 const int32_t* __restrict__ idx, const float4* __restrict__ rowinfo,
+                                                 const int32_t* __restrict__ n_act_p, SplitGeom gm, BwdGeom bg,
+                                                 uint16_t* __restrict__ dZ) {
+  const int i = blockIdx.y;
+  const int col0 = 8 * (blockIdx.x * 256 + threadIdx.x);  // column within the group's dZ row
+  if (col0 >= bg.ldz) return;
+  const int n_act = *n_act_p;
+  if (i >= ((n_act + kBM - 1) / kBM) * kBM) return;
+  const int sc = col0 / bg.S_pad, vl0 = col0 - sc * bg.S_pad;
+  const int sbeg = (bg.c_lo + sc) * gm.S;
+  const int valid_s = max(0, min(gm.S, gm.V - sbeg));
+  float d[8];
+  if (i < n_act) {
+    const float4 ri = rowinfo[i];
+    const float L = ri.x, gi = ri.y;
+    const int yl = __float_as_int(ri.z) - sbeg;
+    // 16-byte aligned: ldzs, S_pad and col0 are multiples of 4
+    const float4* zr = reinterpret_cast<const float4*>(zsave + (size_t)idx[i] * ldzs + (size_t)bg.c_lo * bg.S_pad + col0);
+    const float4 z0 = zr[0], z1 = zr[1];
+    const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int vl = vl0 + e;
+      if (vl < valid_s) {
+        const float p = rlk_exp(z[e] - L);
+        const float delta = (vl == yl) ? 1.f : 0.f;
+        d[e] = gi * (delta - p);
+      } else {
+        d[e] = 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.f;
+  }
+  *reinterpret_cast<u32x4*>(dZ + (size_t)i * bg.ldz + col0) =
+      u32x4{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])};
 }
 
 // MN-mode loader over a row-major matrix: k-row t of k-block kt is matrix

@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(rlk.library_path)
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -159,6 +159,28 @@ def test_gemm_validation():
     assert gemm(M=0, A=None, C=None) == OK
     assert gemm(N=0, B=None, C=None) == OK
     assert gemm(M=0, K=96) == BAD_SHAPE
+
+
+def test_saved_logits_validation():
+    L = rlk.lib()
+    ld = L.rlk_saved_logits_ld(151936)
+    assert ld == 32 * 4800
+    assert L.rlk_saved_logits_ld(4096) == 32 * 128
+    assert L.rlk_saved_logits_ld(0) == 0
+    fs = lambda z=FAKE, ldz=ld, lse=FAKE, T=64: L.rlk_linear_logp_fwd_save(
+        FAKE, FAKE, FAKE, T, 4096, 151936, -100, FAKE, lse, z, ldz, FAKE, 1 << 40, None)
+    assert fs(z=None) == NULL_ARG
+    assert fs(lse=None) == NULL_ARG
+    assert fs(ldz=ld - 4) == BAD_SHAPE
+    assert fs(ldz=ld + 2) == BAD_SHAPE
+    assert fs(z=MISALIGNED) == BAD_ALIGN
+    assert fs(T=0, z=None) == OK
+    bs = lambda z=FAKE, ldz=ld, T=64: L.rlk_linear_logp_bwd_saved(
+        FAKE, FAKE, FAKE, FAKE, FAKE, z, ldz, T, 4096, 151936, -100, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert bs(z=None) == NULL_ARG
+    assert bs(ldz=100) == BAD_SHAPE
+    assert bs(z=MISALIGNED) == BAD_ALIGN
+    assert bs(T=0, z=None, ldz=0) == OK
 
 
 def test_binding_refuses_host_tensors():
