@@ -429,6 +429,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
+  // this wave's 128 rows all active and 128 columns all inside the split
+  // (wave-uniform; false only on the last row tile and last column tile)
+  const int wc0 = j * kBN + 128 * wn;  // first column of the wave within the split
+  const bool full = i0 + 128 * wm + 128 <= n_act && wc0 + 128 <= valid_s;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
     const int i = i0 + acc_row(wm, mi, lane);
@@ -436,22 +440,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const float L = ri[mi].x, gi = ri[mi].y;
     const int yl = __float_as_int(ri[mi].z) - sbeg;  // target column within the split
     uint16_t* drow = dzs + (size_t)i * a.bg.ldz;
+    // does this lane hold its row's target column?  (rare)
+    const int tl = yl - wc0;
+    const bool hit = tl >= 0 && tl < 128 && ((tl >> 2) & 1) == (lane >> 5);
+    if (full && !__builtin_amdgcn_ballot_w64(hit)) {
+      // every element is off-target, active and inside the split: the same
+      // formula with delta = 0, without the per-element tests
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
+      for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform
-        const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
-        float d[4];
+        for (int q = 0; q < 4; ++q) {
+          const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
+          float d[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int vl = vl0 + e;
-          const float p = rlk_exp(acc.c[mi][ni][4 * q + e] - L);
-          const float delta = (vl == yl) ? 1.f : 0.f;
-          d[e] = (rvalid && vl < valid_s) ? gi * (delta - p) : 0.f;
+          for (int e = 0; e < 4; ++e) d[e] = gi * (0.f - rlk_exp(acc.c[mi][ni][4 * q + e] - L));
+          *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
         }
-        *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-      }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform
+          const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
+          float d[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int vl = vl0 + e;
+            const float p = rlk_exp(acc.c[mi][ni][4 * q + e] - L);
+            const float delta = (vl == yl) ? 1.f : 0.f;
+            d[e] = (rvalid && vl < valid_s) ? gi * (delta - p) : 0.f;
+          }
+          *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+        }
+    }
   }
 }
 
