@@ -40,6 +40,9 @@ WORKLOADS = {
     "qwen3_8b_fwd_bwd_saved": (4096, 4096, 151936, 0.15, True,
                                "linear_logp fwd+bwd, save-logits variant (fp32 logits kept between the passes, "
                                "no recompute), Qwen3-8B-shaped LM head (T=4096, H=4096, V=151936, 15% rows ignored)"),
+    "qwen3_8b_tp2_partials": (4096, 4096, 151936, 0.15, False,
+                              "linear_logp forward as two vocabulary shards of 75968 rows on one GPU "
+                              "(rlk_lse_partial x 2 + rlk_lse_merge), Qwen3-8B-shaped LM head"),
     "qwen3_30b_a3b_fwd_bwd": (16384, 2048, 151936, 0.15, True,
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
 }
@@ -151,6 +154,13 @@ def traffic_from(run_dir, command):
         print(f"{k}: fetch {fb / 1e9:.3f} GB, write {wb / 1e9:.3f} GB per launch", flush=True)
     print(f"calibration {ck}: fetch scale {f_scale:.4f}, write scale {w_scale:.4f}", flush=True)
     return rows
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    # the GFX clock under load is not exposed here; profiles/ derives it from
+    # GRBM_GUI_ACTIVE cycles over kernel time
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count}
 
 
 def gemm_bench(args):
@@ -299,8 +309,18 @@ def main():
 
     saved = args.workload.endswith("_saved")
     zsave = torch.empty((T, rlk.saved_logits_ld(V)), dtype=torch.float32, device=dev) if saved else None
+    sharded = args.workload.endswith("_tp2_partials")
+    half = V // 2
+    if sharded:
+        W_sh = [W[:half].contiguous(), W[half:].contiguous()]
+        parts = torch.empty((2, T, 4), dtype=torch.float32, device=dev)
 
     def step():
+        if sharded:
+            for r in range(2):
+                rlk.lse_partial(h, W_sh[r], y, r * half, V, ws=ws_f, out=parts[r])
+            rlk.lse_merge(parts, y)
+            return
         if saved:
             logp, lse, _ = rlk.linear_logp_fwd_save(h, W, y, ws=ws_f, zsave=zsave)
             rlk.linear_logp_bwd_saved(h, W, y, lse, g, zsave, ws=ws_b)
@@ -319,15 +339,19 @@ def main():
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     rlk.profile_begin()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        step_ev[k].record(stream)
         step()
+    step_ev[args.steps].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    per_step = sorted(step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps))
     kern = rlk.profile_end()
     peak_reserved = torch.cuda.max_memory_reserved()
     if args.copy_calibration:
@@ -366,7 +390,7 @@ def main():
     }
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "qwen3_8b_fwd_bwd" else f"{args.workload}: tokens/s",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -380,6 +404,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "H": H, "V": V, "active_rows": T_act,
                    "ignore_index": -100, "parallelism": "single GPU"},
+        "step_ms_median_p10_p90": [per_step[len(per_step) // 2], per_step[len(per_step) // 10],
+                                   per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)]],
+        "device": device_info(torch),
         "mfma_frac_step": flops_step / (ms * 1e-3) / PEAK_BF16,
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "roofline": roofline,

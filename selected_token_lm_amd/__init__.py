@@ -231,7 +231,7 @@ def linear_logp_bwd_saved(h, W, y, lse, g, zsave, ignore_index: int = IGNORE_IND
 
 
 def lse_partial(h, W_shard, y, vocab_start: int, V_global: int,
-                ignore_index: int = IGNORE_INDEX, ws=None):
+                ignore_index: int = IGNORE_INDEX, ws=None, out=None):
     """Per-row statistics of the range [vocab_start, vocab_start + len(W_shard)).
 
     Returns a float32 tensor [T, 4] holding (m, s, z_target, owned) per row;
@@ -240,7 +240,10 @@ def lse_partial(h, W_shard, y, vocab_start: int, V_global: int,
     h, W_shard, y = _prep(h, W_shard, y)
     T, H = h.shape
     n_rows = W_shard.shape[0]
-    out = torch.empty((T, 4), dtype=torch.float32, device=h.device)
+    if out is None:
+        out = torch.empty((T, 4), dtype=torch.float32, device=h.device)
+    elif out.shape != (T, 4) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [T, 4] tensor")
     if ws is None:
         ws, n = _workspace(OP_PARTIAL, T, H, V_global, h.device)
     else:
