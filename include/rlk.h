@@ -201,6 +201,27 @@ rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts,
                          const int32_t* y, int64_t T, int32_t ignore_index,
                          float* logp, float* lse, void* stream);
 
+/* Per-token RL objective on the selected log-probability, and its
+ * derivative as the upstream gradient of rlk_linear_logp_bwd.  The pages
+ * say the selected logp exists for the importance ratio, clipping and KL
+ * terms of PPO / GRPO ("vLLM RL-Kernel v0.1.0 ...", opening section;
+ * "Announcing RL-Kernel for vime", section "Vision"), and name the k3 KL
+ * estimator; they print no formulas, so the standard ones are used:
+ *     r = e(logp - logp_old),  c = min(max(r, 1 - eps_low), 1 + eps_high)
+ *     loss = scale * ( -min(r*adv, c*adv) + beta * ((e(d) - d) - 1) ),  d = logp_ref - logp
+ *     g    = scale * ( (r*adv <= c*adv ? -r*adv : 0) + beta * (1 - e(d)) )
+ * fp32, each operation rounded once in the order written, e() the
+ * library's exp.  Rows with y == ignore_index get loss = g = 0.
+ *   logp, logp_old, adv   fp32 [T]   (logp from rlk_linear_logp_fwd)
+ *   logp_ref              fp32 [T]   reference policy; may be NULL if beta == 0
+ *   loss, g               fp32 [T] out; either may be NULL
+ * Requires 0 <= eps_low < 1, eps_high >= 0, beta >= 0.  Pointers need only
+ * the natural 4-byte alignment. */
+rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const float* adv,
+                             const float* logp_ref, const int32_t* y, int64_t T,
+                             int32_t ignore_index, float eps_low, float eps_high, float beta,
+                             float scale, float* loss, float* g, void* stream);
+
 /* Output element types of rlk_gemm_bf16_nt. */
 enum { RLK_DT_F32 = 0, RLK_DT_BF16 = 1 };
 

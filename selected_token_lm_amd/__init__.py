@@ -26,7 +26,7 @@ __all__ = [
     "IGNORE_INDEX", "RlkError", "lib", "library_path", "contract_version",
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
     "lse_merge", "linear_logp", "gemm_bf16_nt", "linear_logp_fwd_save", "linear_logp_bwd_saved",
-    "saved_logits_ld", "profile_begin", "profile_end",
+    "saved_logits_ld", "rl_token_loss", "profile_begin", "profile_end",
 ]
 
 IGNORE_INDEX = -100
@@ -63,6 +63,9 @@ _SIGNATURES = {
     "rlk_linear_logp_bwd_saved": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                          _c_void_p, _i64, _i64, _i64, _i64, _i32, _c_void_p,
                                          _c_void_p, _c_void_p, _size, _c_void_p]),
+    "rlk_rl_token_loss": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                                 ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                 _c_void_p, _c_void_p, _c_void_p]),
     "rlk_profile_begin": (_i32, []),
     "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
 }
@@ -291,6 +294,27 @@ def gemm_bf16_nt(A, B, out_dtype=torch.float32):
                                   0 if out_dtype == torch.float32 else 1, _stream()),
            "rlk_gemm_bf16_nt")
     return C[:, :N] if ldc != N else C
+
+
+def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float = 0.2,
+                  beta: float = 0.0, logp_ref=None, scale: float = 1.0,
+                  ignore_index: int = IGNORE_INDEX):
+    """Per-token clipped-surrogate + k3-KL loss and g = dloss/dlogp, fp32 [T] each."""
+    def f32(x):
+        if not x.is_cuda:
+            raise ValueError("inputs must be device tensors")
+        return x.to(torch.float32).contiguous()
+    logp, logp_old, adv = f32(logp), f32(logp_old), f32(adv)
+    ref = f32(logp_ref) if logp_ref is not None else None
+    y = (y.to(torch.int32) if y.dtype != torch.int32 else y).contiguous()
+    T = logp.shape[0]
+    loss = torch.empty(T, dtype=torch.float32, device=logp.device)
+    g = torch.empty(T, dtype=torch.float32, device=logp.device)
+    _check(lib().rlk_rl_token_loss(_ptr(logp), _ptr(logp_old), _ptr(adv), _ptr(ref), _ptr(y), T,
+                                   ignore_index, eps_low, eps_high, beta, scale, _ptr(loss), _ptr(g),
+                                   _stream()),
+           "rlk_rl_token_loss")
+    return loss, g
 
 
 def profile_begin():

@@ -587,6 +587,35 @@ rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, 
   return ok();
 }
 
+rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const float* adv, const float* logp_ref,
+                             const int32_t* y, int64_t T, int32_t ignore_index, float eps_low, float eps_high,
+                             float beta, float scale, float* loss, float* g, void* stream) {
+  if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
+  if (!(eps_low >= 0.f && eps_low < 1.f) || !(eps_high >= 0.f) || !(beta >= 0.f) || !(scale == scale))
+    return fail(RLK_ERR_BAD_ARG, "need 0 <= eps_low < 1, eps_high >= 0, beta >= 0, scale not NaN");
+  if (T == 0) return ok();
+  if (!logp || !logp_old || !adv || !y || (beta != 0.f && !logp_ref))
+    return fail(RLK_ERR_NULL_ARG, "logp, logp_old, adv, y (and logp_ref when beta > 0) are required");
+  if (!loss && !g) return ok();
+  RLK_TRY(check_device());
+  rlk::RlLossArgs ra;
+  ra.logp = logp;
+  ra.logp_old = logp_old;
+  ra.adv = adv;
+  ra.logp_ref = logp_ref;
+  ra.y = y;
+  ra.T = (int)T;
+  ra.ignore_index = ignore_index;
+  ra.eps_low = eps_low;
+  ra.eps_high = eps_high;
+  ra.beta = beta;
+  ra.scale = scale;
+  ra.loss = loss;
+  ra.g = g;
+  RLK_LAUNCH(rl_token_loss, dim3((unsigned)ceil_div(T, 256)), dim3(256), static_cast<hipStream_t>(stream), ra);
+  return ok();
+}
+
 rlk_status rlk_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof_recs) {

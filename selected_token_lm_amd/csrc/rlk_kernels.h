@@ -12,6 +12,8 @@
 //                        grad_h: fp32 accumulator += dz W; bf16 after the last group
 //                        grad_W: rows of the group = dz^T h  (K = active rows)
 //   zero_rows          zero grad_h rows of inactive rows
+// RL objective (O(T)):
+//   rl_token_loss      clipped surrogate + k3 KL per token, and dL/dlogp
 // Dense product (same engine):
 //   gemm_tiles         C = A B^T, one MFMA chain per element
 #pragma once
@@ -733,6 +735,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (id >= 0) gradw_tile(wa, id, n_act, lds);
 }
 
+
+// ---------------------------------------------------------------------------
+// Per-token RL objective on the selected logp (PPO / GRPO clipped surrogate
+// and k3 KL to a reference), with its derivative g = dL/dlogp ready for the
+// backward.  Every operation is a separately rounded fp32 operation in the
+// order written; exp is the library's e(x).  One thread per token.
+// ---------------------------------------------------------------------------
+struct RlLossArgs {
+  const float* logp;
+  const float* logp_old;
+  const float* adv;
+  const float* logp_ref;  // may be NULL when beta == 0
+  const int32_t* y;
+  int T;
+  int ignore_index;
+  float eps_low, eps_high, beta, scale;
+  float* loss;  // may be NULL
+  float* g;     // may be NULL
+};
+
+__global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  float L = 0.f, gt = 0.f;
+  if (a.y[t] != a.ignore_index) {
+    const float lp = a.logp[t], A = a.adv[t];
+    const float r = rlk_exp(lp - a.logp_old[t]);
+    const float c = fminf(fmaxf(r, 1.f - a.eps_low), 1.f + a.eps_high);
+    const float ra = r * A, ca = c * A;
+    L = -fminf(ra, ca);
+    gt = (ra <= ca) ? -ra : 0.f;
+    if (a.beta != 0.f) {
+      const float d = a.logp_ref[t] - lp;
+      const float ed = rlk_exp(d);
+      L = L + a.beta * ((ed - d) - 1.f);
+      gt = gt + a.beta * (1.f - ed);
+    }
+    L = a.scale * L;
+    gt = a.scale * gt;
+  }
+  if (a.loss) a.loss[t] = L;
+  if (a.g) a.g[t] = gt;
+}
 
 // ---------------------------------------------------------------------------
 // Deterministic dense product C = A B^T on the same tile engine: every

@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(rlk.library_path)
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -181,6 +181,19 @@ def test_saved_logits_validation():
     assert bs(ldz=100) == BAD_SHAPE
     assert bs(z=MISALIGNED) == BAD_ALIGN
     assert bs(T=0, z=None, ldz=0) == OK
+
+
+def test_rl_loss_validation():
+    L = rlk.lib()
+    f = lambda T=8, elo=0.2, ehi=0.2, beta=0.0, ref=None, lp=FAKE: L.rlk_rl_token_loss(
+        lp, FAKE, FAKE, ref, FAKE, T, -100, elo, ehi, beta, 1.0, FAKE, FAKE, None)
+    assert f(lp=None) == NULL_ARG
+    assert f(beta=0.1) == NULL_ARG          # beta > 0 needs logp_ref
+    assert f(elo=1.0) == BAD_ARG
+    assert f(elo=-0.1) == BAD_ARG
+    assert f(beta=-1.0) == BAD_ARG
+    assert f(T=-1) == BAD_SHAPE
+    assert f(T=0, lp=None) == OK
 
 
 def test_binding_refuses_host_tensors():
