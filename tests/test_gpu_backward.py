@@ -137,3 +137,15 @@ def test_split_grouping_changes_no_bit(monkeypatch):
         gh2, gW2 = rlk.linear_logp_bwd(h, W, y, lse, g)
         torch.cuda.synchronize()
         assert torch.equal(gh, gh2) and torch.equal(gW, gW2), mb
+
+
+@pytest.mark.parametrize("T,H,V", [(3, 65536, 600), (5, 64, 8_000_000)])
+def test_maximum_hidden_and_vocabulary(T, H, V):
+    say(f"bwd max sizes T={T} H={H} V={V}")
+    inp = synth.make_inputs(T, H, V, 0.0)
+    _, logp, lse, gh, gW = fwd_bwd(inp)
+    ref_gh, ref_gW = oracle.backward(inp.h, inp.W, inp.y, inp.g)
+    e_h = rel_l2(to64(gh), ref_gh)
+    e_W = rel_l2(to64(gW), ref_gW)
+    say(f"  relL2 grad_h={e_h:.3e} grad_W={e_W:.3e}")
+    assert e_h <= GRAD_RTOL and e_W <= GRAD_RTOL

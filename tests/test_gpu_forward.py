@@ -253,3 +253,12 @@ def test_qwen3_8b_heavy_tail_rebatch_bitwise(q8b):
         r = torch.from_numpy(rows).to(DEV)
         got, gl = rlk.linear_logp_fwd(h8[r], W, y[r])
         assert torch.equal(got, ref[r]) and torch.equal(gl, ref_lse[r]), len(rows)
+
+
+@pytest.mark.parametrize("T,H,V", [(3, 65536, 600), (5, 64, 8_000_000)])
+def test_maximum_hidden_and_vocabulary(T, H, V):
+    # the largest H and V the library accepts (32-bit offsets at their limits)
+    say(f"max sizes T={T} H={H} V={V}")
+    inp = synth.make_inputs(T, H, V, 0.0)
+    logp, lse = run_fwd(inp)
+    check_vs_oracle(inp, logp, lse)

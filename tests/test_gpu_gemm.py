@@ -111,3 +111,12 @@ def test_empty_products():
     B = torch.zeros((5, 64), dtype=torch.bfloat16, device=DEV)
     assert rlk.gemm_bf16_nt(A, B).shape == (0, 5)
     assert rlk.gemm_bf16_nt(B, A).shape == (5, 0)
+
+
+def test_maximum_k():
+    M, N, K = 3, 5, 1 << 20
+    say(f"[gemm] max K: M={M} N={N} K={K}")
+    A, B = operands(M, N, K, seed=41)
+    C = rlk.gemm_bf16_nt(bf16_dev(A), bf16_dev(B))
+    torch.cuda.synchronize()
+    check(C, A, B)
