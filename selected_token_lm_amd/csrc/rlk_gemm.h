@@ -36,11 +36,11 @@
 // Both LDS layouts are XOR-swizzled so that the 16 lanes served per LDS
 // cycle hit distinct banks.
 //
-// Pipelined: k-blocks of 64 are loaded straight from global memory into two
-// LDS stages, one k-block ahead of the MFMAs.  A K-mode row contributes 128
-// contiguous bytes per k-block (one full cache line), which halves the
-// number of memory requests per byte compared with 32-wide k-blocks: the
-// direct loads are limited by the requests a CU can keep in flight.
+// Pipelined: k-blocks of 64 are loaded straight from global memory into a
+// ring of five 32 KB operand-tile slots in LDS (gemm256 below), 1 to 1.5
+// k-blocks ahead of the MFMAs.  A K-mode row contributes 128 contiguous
+// bytes per k-block (one full cache line), which halves the number of
+// memory requests per byte compared with 32-wide k-blocks.
 #pragma once
 
 #include "rlk_device.h"
@@ -114,8 +114,7 @@ __device__ __forceinline__ FragOffs frag_offs(int r0, int lane) {
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Fragment J, k step kk of the tile at `tile` (a pointer into the kernel's
-// LDS array: deriving every read from that array lets the compiler see that
-// reads of one stage do not alias the direct loads into the other one).
+// LDS array, so that every read derives from that array).
 template <bool MN, int J>
 __device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, int kk) {
   const char* base = reinterpret_cast<const char*>(tile);
@@ -145,8 +144,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Written as inline assembly (uniform base in scalar registers, 32-bit lane
 // offset): the compiler then does not know these loads write LDS, so it adds
-// no waits of its own before later LDS reads (it cannot tell the stages
-// apart for every read form).  The kernels order them explicitly: a stage is
+// no waits of its own before later LDS reads (it cannot tell the slots
+// apart for every read form).  gemm256 orders them explicitly: a slot is
 // read only after wait_vm and a barrier, and refilled only after a barrier
 // that follows the last reads of it.
 // m0: LDS byte address of the instruction's 1 KB (wave-uniform).
@@ -233,9 +232,8 @@ __device__ __forceinline__ const bf16x8& frag(const Frags& f) {
   return frag<J>(const_cast<Frags&>(f));
 }
 
-// Fragment J of k step kk (J < 4: A block J, else B block J - 4) from the
-// stage at LDS byte address st.
-// (tA, tB: the k-block's A and B tiles in LDS.)
+// Fragment J of k step kk (J < 4: A block J, else B block J - 4) of the
+// k-block whose A and B tiles are at tA, tB in LDS.
 template <bool A_MN, bool B_MN, int J>
 __device__ __forceinline__ void load_frag(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
                                           int kk, Frags& g) {
