@@ -66,24 +66,66 @@ GEMM_WORKLOADS = {
 GEMM_KERNELS = {"fwd_tiles": 1, "dz_tiles": 1, "grad_tiles": 2, "gemm_tiles": 1}
 
 
-def source_digest():
+def _elf_sections(data):
+    """{name: (address, bytes)} of the sections of a 64-bit little-endian ELF image."""
+    import struct
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    sec = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = data[sec[shstrndx][4]:sec[shstrndx][4] + sec[shstrndx][5]]
+    return {names[s[0]:names.index(b"\0", s[0])].decode(): (s[3], data[s[4]:s[4] + s[5]]) for s in sec}
+
+
+def _gfx950_code_object(lib_path):
+    """The gfx950 code object (an ELF image) inside the library's offload bundle."""
+    import struct
+    with open(lib_path, "rb") as f:
+        bundle = _elf_sections(f.read())[".hip_fatbin"][1]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    assert bundle.startswith(magic), "uncompressed offload bundle expected"
+    n, = struct.unpack_from("<Q", bundle, len(magic))
+    pos = len(magic) + 8
+    for _ in range(n):
+        off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
+        triple = bundle[pos + 24:pos + 24 + tlen].decode()
+        pos += 24 + tlen
+        if "gfx950" in triple:
+            return bundle[off:off + size]
+    raise KeyError("gfx950")
+
+
+def kernel_digest(kernel):
+    """Digest of the machine code of the library's kernels named `kernel`
+    (every template instance): it changes exactly when that kernel's code
+    does, whatever else changes in the sources."""
+    import struct
+    import selected_token_lm_amd as rlk
+    co = _gfx950_code_object(rlk.library_path)
+    secs = _elf_sections(co)
+    text_addr, text = secs[".text"]
+    strtab = secs[".strtab"][1]
+    symtab = secs[".symtab"][1]
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "selected_token_lm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    found = []
+    for i in range(0, len(symtab), 24):
+        name_off, info, _, _, value, size = struct.unpack_from("<IBBHQQ", symtab, i)
+        name = strtab[name_off:strtab.index(b"\0", name_off)].decode()
+        if (info & 0xF) == 2 and size and f"{len(kernel)}{kernel}" in name:  # STT_FUNC, mangled name
+            found.append((name, text[value - text_addr:value - text_addr + size]))
+    for name, code in sorted(found):
+        h.update(name.encode() + code)
+    return h.hexdigest()[:16] if found else None
 
 
-def traffic_for(kernel, digest):
+def traffic_for(kernel):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the kernel's current machine code; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != digest:
+    if rec.get("kernel_digest") != kernel_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -138,14 +180,13 @@ def traffic_from(run_dir, command):
     ck = copy[0]
     f_scale = COPY_BYTES / (fetch[ck][0] * 1024.0)
     w_scale = COPY_BYTES / (write[ck][0] * 1024.0)
-    digest = source_digest()
     rows = []
     for k in GEMM_KERNELS:
         if k not in fetch or k not in write:
             continue
         fb = fetch[k][0] * 1024.0 * f_scale
         wb = write[k][0] * 1024.0 * w_scale
-        rec = {"kernel": k, "source_digest": digest, "bytes_per_launch": fb + wb, "fetch_bytes": fb,
+        rec = {"kernel": k, "kernel_digest": kernel_digest(k), "bytes_per_launch": fb + wb, "fetch_bytes": fb,
                "write_bytes": wb, "dispatches": fetch[k][1], "calibration_kernel": ck,
                "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
         with open(os.path.join(ROOT, "profiles", f"traffic_{k}.json"), "w") as f:
@@ -223,11 +264,11 @@ def gemm_bench(args):
         "config": {"workload": desc, "M": M, "N": N, "K": K},
         "roofline": {"bound": "mfma", "kernel": "gemm_tiles", "achieved": achieved / 1e12,
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
-                     "traffic": traffic_for("gemm_tiles", source_digest()), "flops_per_launch": flops,
+                     "traffic": traffic_for("gemm_tiles"), "flops_per_launch": flops,
                      "avg_launch_ms": k_ms},
         "context": {"vendor_bf16_gemm": "torch.matmul (hipBLASLt), same operands, not deterministic by contract",
                     "vendor_ms": vendor_ms, "vendor_tflops": flops / (vendor_ms * 1e-3) / 1e12},
-        "source_digest": source_digest(),
+        "kernel_digest": kernel_digest("gemm_tiles"),
     }
     print(json.dumps(out), flush=True)
 
@@ -364,7 +405,6 @@ def main():
     # save-logits variant), grad_W, grad_h
     flops_step = 2.0 * T_act * H * V * ((3 if saved else 4) if do_bwd else 1)
 
-    digest = source_digest()
     kernels = {}
     per_step_flops = 2.0 * T_act * H * V
     for name, (n, tot) in sorted(kern.items(), key=lambda kv: -kv[1][1]):
@@ -384,7 +424,7 @@ def main():
         "peak": PEAK_BF16 / 1e12,
         "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16,
-        "traffic": traffic_for(dom, digest),
+        "traffic": traffic_for(dom),
         "flops_per_launch": dom_fl,
         "avg_launch_ms": kernels[dom]["avg_ms"],
     }
@@ -414,7 +454,7 @@ def main():
         "workspace_bytes": int(ws_f.numel() + (ws_b.numel() if do_bwd else 0)
                                + (zsave.numel() * 4 if saved else 0)),
         "peak_reserved_delta_mb": (peak_reserved - reserved0) / 2**20,
-        "source_digest": digest,
+        "kernel_digest": kernel_digest(dom),
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_rows} rows)", file=sys.stderr, flush=True)
