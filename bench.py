@@ -397,6 +397,9 @@ def main():
     peak_reserved = torch.cuda.max_memory_reserved()
     if args.copy_calibration:
         copy_calibration(dev)
+    # the part's MFMA ceiling on this machine right now (pure MFMA, random
+    # operands, no memory traffic): context for the roofline fraction
+    ceiling = rlk.bench_mfma_ceiling()
 
     ms_wall = (t1 - t0) * 1e3 / args.steps
     ms_ev = ev0.elapsed_time(ev1) / args.steps
@@ -451,6 +454,10 @@ def main():
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "roofline": roofline,
         "kernels": kernels,
+        "mfma_ceiling": {"what": "pure v_mfma_f32_32x32x16_bf16 loop on random bf16 operands, no memory traffic, "
+                                 "same box after the timed steps (rlk_bench_mfma_ceiling)",
+                         "best_tflops": ceiling["best_tflops"], "median_tflops": ceiling["median_tflops"],
+                         "dominant_kernel_frac_of_ceiling": achieved / 1e12 / ceiling["median_tflops"]},
         "workspace_bytes": int(ws_f.numel() + (ws_b.numel() if do_bwd else 0)
                                + (zsave.numel() * 4 if saved else 0)),
         "peak_reserved_delta_mb": (peak_reserved - reserved0) / 2**20,

@@ -246,6 +246,18 @@ enum { RLK_DT_F32 = 0, RLK_DT_BF16 = 1 };
 rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                             void* C, int64_t ldc, int32_t c_dtype, void* stream);
 
+/* Benchmark only (computes nothing of the operator): runs `blocks`
+ * workgroups of 4 waves, each wave issuing iters * 64
+ * v_mfma_f32_32x32x16_bf16 on a 128 x 128 accumulator tile with operands
+ * cycled through 4 register sets of random bf16 data, and no memory traffic
+ * in the loop: the MFMA throughput the part sustains under its power limit
+ * with realistic operand toggling (2 * 32 * 32 * 16 FLOP per instruction).
+ *   src  bf16 device buffer of 32 * 256 * 8 values (random; 16-byte aligned)
+ *   out  fp32 [blocks * 256] out (sums of the accumulators, so nothing is
+ *        optimised away) */
+rlk_status rlk_bench_mfma_ceiling(const void* src, float* out, int32_t blocks, int32_t iters,
+                                  void* stream);
+
 /* Per-kernel timing for benchmarks; computes nothing.  After
  * rlk_profile_begin(), every kernel the library launches (on any stream) is
  * bracketed by two HIP events recorded on that stream.  rlk_profile_end()

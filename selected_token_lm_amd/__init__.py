@@ -66,6 +66,7 @@ _SIGNATURES = {
     "rlk_rl_token_loss": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                  _c_void_p, _c_void_p, _c_void_p]),
+    "rlk_bench_mfma_ceiling": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p]),
     "rlk_profile_begin": (_i32, []),
     "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
 }
@@ -315,6 +316,28 @@ def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float 
                                    _stream()),
            "rlk_rl_token_loss")
     return loss, g
+
+
+def bench_mfma_ceiling(blocks: int = 256, iters: int = 4096, repeats: int = 3):
+    """Benchmark only: TFLOP/s of a pure v_mfma_f32_32x32x16_bf16 loop on random
+    operands (no memory traffic), best and median of `repeats` timed launches."""
+    gen = torch.Generator(device="cuda").manual_seed(12345)
+    src = torch.randn(32 * 256 * 8, device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = 2.0 * 32 * 32 * 16 * 64 * iters * 4 * blocks
+    times = []
+    for r in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(lib().rlk_bench_mfma_ceiling(_ptr(src), _ptr(out), blocks, iters, _stream()),
+               "rlk_bench_mfma_ceiling")
+        e1.record()
+        torch.cuda.synchronize()
+        if r:  # the first launch warms up
+            times.append(e0.elapsed_time(e1))
+    times.sort()
+    return {"best_tflops": flops / times[0] / 1e9, "median_tflops": flops / times[len(times) // 2] / 1e9,
+            "launch_ms": times}
 
 
 def profile_begin():

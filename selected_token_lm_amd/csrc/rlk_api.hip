@@ -616,6 +616,16 @@ rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const flo
   return ok();
 }
 
+rlk_status rlk_bench_mfma_ceiling(const void* src, float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (blocks <= 0 || blocks > 65536 || iters <= 0) return fail(RLK_ERR_BAD_ARG, "blocks in [1, 65536], iters > 0");
+  if (!src || !out) return fail(RLK_ERR_NULL_ARG, "src and out are required");
+  if (!aligned16(src)) return fail(RLK_ERR_BAD_ALIGNMENT, "src must be 16-byte aligned");
+  RLK_TRY(check_device());
+  RLK_LAUNCH(mfma_ceiling, dim3((unsigned)blocks), dim3(256), static_cast<hipStream_t>(stream),
+             static_cast<const rlk::u32x4*>(src), out, (int)iters);
+  return ok();
+}
+
 rlk_status rlk_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof_recs) {

@@ -780,6 +780,41 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Benchmark only: the MFMA ceiling of the part under realistic operands.
+// Each wave holds the engine's 128 x 128 fp32 tile (16 blocks of 32 x 32 in
+// accumulator registers) and issues nothing but v_mfma_f32_32x32x16_bf16,
+// cycling through 4 register sets of the caller's random bf16 data so the
+// matrix cores see realistic bit toggling; no memory traffic in the loop.
+// src: 32 * 256 16-byte pieces; out: one float per thread (keeps the result).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ceiling(
+    const u32x4* __restrict__ src, float* __restrict__ out, int iters) {
+  bf16x8 fa[4][4], fb[4][4];  // [set][fragment]
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fa[s][j] = __builtin_bit_cast(bf16x8, src[(s * 8 + j) * 256 + threadIdx.x]);
+      fb[s][j] = __builtin_bit_cast(bf16x8, src[(s * 8 + 4 + j) * 256 + threadIdx.x]);
+    }
+  f32x16 c[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) c[j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j & 3], fa[s][j >> 2], c[j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += c[j][i];
+  out[blockIdx.x * 256 + threadIdx.x] = t;
+}
+
+// ---------------------------------------------------------------------------
 // Deterministic dense product C = A B^T on the same tile engine: every
 // element is one MFMA chain over k ascending, whatever the tile it falls in,
 // so a row of C depends only on its row of A (and B).  Tile id: (row tile of

@@ -30,7 +30,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(rlk.library_path)
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
