@@ -17,7 +17,6 @@ LIB = os.path.join(HERE, "librlk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["rlk_api.hip"]
-HEADERS = ["rlk_device.h", "rlk_kernels.h"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -40,7 +39,12 @@ FLAGS = [
 def build(verbose: bool = True) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    # RLK_WAVES=8: two waves per SIMD in the tile engine (same results; four
+    # is the default and the faster build on MI355X)
+    waves = os.environ.get("RLK_WAVES", "4")
+    if waves not in ("4", "8"):
+        raise ValueError(f"RLK_WAVES must be 4 or 8, not {waves!r}")
+    cmd = [HIPCC, *FLAGS, f"-DRLK_WAVES={waves}", "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

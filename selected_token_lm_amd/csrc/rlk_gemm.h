@@ -6,10 +6,12 @@
 // operand layouts) never changes a result bit: every element is the same
 // chain of MFMA steps over the same k values.
 //
-// 256 threads = 4 waves, one per SIMD; wave w owns rows 128*(w & 1) .. +128
-// and columns 128*(w >> 1) .. +128 of the tile, as 4 x 4 blocks of 32 x 32
-// (256 accumulator registers).  A 128-column vocabulary chunk of a row
-// therefore lives inside one wave.
+// kWaves = 4 (one wave per SIMD) or 8 (two per SIMD, RLK_WAVES=8 at build
+// time): wave w owns rows R*(w % (kWaves/2)) .. +R, R = 512 / kWaves, and
+// columns 128*(w / (kWaves/2)) .. +128 of the tile, as (R/32) x 4 blocks of
+// 32 x 32 (256 or 128 accumulator registers).  A 128-column vocabulary chunk
+// of a row therefore lives inside one wave, and every output element is the
+// same MFMA chain whatever the wave count.
 //
 // MFMA register layouts (32x32x16 bf16, D = X * Y^T):
 //   X operand, lane l: row (l & 31), k = 8*(l >> 5) + 0..7 of the k step
@@ -52,12 +54,21 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // registers in private memory)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
-constexpr int kMI = 4, kNI = 4;            // 32 x 32 blocks per wave
+#ifndef RLK_WAVES
+#define RLK_WAVES 4
+#endif
+constexpr int kWaves = RLK_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "four or eight waves per tile");
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 64 * kWaves;
+constexpr int kWM = kWaves / 2;            // waves along the tile's rows (two along its columns)
+constexpr int kWaveRows = kBM / kWM;       // tile rows per wave
+constexpr int kMI = kWaveRows / 32, kNI = 4;  // 32 x 32 blocks per wave
+constexpr int kMma = kMI * kNI;            // MFMAs per wave per k step
+constexpr int kReads = kMI + kNI;          // fragment reads per wave per k step
 constexpr int kKK = kBK / 16;              // MFMA k steps per k-block
 constexpr int kSegs = kBK / 8;             // 16-byte pieces per K-mode row
-constexpr int kDma = kBK / 8;              // direct-load instructions per wave per operand per k-block
 constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (32 KB)
+constexpr int kDma = kTileU4 / 64 / kWaves;  // direct-load instructions per wave per operand per k-block
 constexpr int kTileU4Check = 256 * kBK / 8;
 static_assert(kTileU4 == kTileU4Check, "tile = 256 rows x kBK bf16");
 constexpr int kSlots = 5;                  // LDS tile slots (a ring of operand tiles)
@@ -73,6 +84,12 @@ __device__ __forceinline__ int slot_k(int row, int seg) { return row * kSegs + (
 __device__ __forceinline__ int slot_mn(int krow, int p) {
   return krow * 32 + ((((p >> 2) ^ (krow & 7)) << 2) | (p & 3));
 }
+
+// Position of wave w in the tile's wave grid: row group wave_m (kWaveRows
+// rows each), column group wave_n (128 columns each).
+static_assert(kWM == 2 || kWM == 4, "power-of-two wave grid");
+__device__ __forceinline__ int wave_m(int w) { return w & (kWM - 1); }
+__device__ __forceinline__ int wave_n(int w) { return w >> (kWM == 2 ? 1 : 2); }
 
 // ---- operand fragments from LDS ----------------------------------------------
 // Per-lane LDS byte offsets of one operand's fragments within its tile,
@@ -135,8 +152,8 @@ __device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, 
 // lane l at byte 16 l.  Instruction i of wave w covers tile slots
 // 64 (kDma w + i) .. +64, so lane l of it fills slot s = 64 (kDma w + i) + l and
 // fetches the global piece that the swizzled layout puts there:
-//   K mode : row 64 w + 8 i + (l >> 3), piece (l & 7) ^ ((row >> 1) & 7)
-//   MN mode: k-row 16 w + 2 i + (l >> 5),
+//   K mode : row 8 (kDma w + i) + (l >> 3), piece (l & 7) ^ ((row >> 1) & 7)
+//   MN mode: k-row 2 (kDma w + i) + (l >> 5),
 //            piece ((((l & 31) >> 2) ^ (k-row & 7)) << 2) | (l & 3)
 // (i = 0 .. kDma-1).
 // No registers hold the staged data.
@@ -157,10 +174,10 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t m
 }
 
 // K-mode row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_k_row(int i) { return 64 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int dma_k_row(int i) { return 8 * kDma * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 7) ^ ((row >> 1) & 7); }
 // MN-mode k-row and piece of instruction i for this thread
-__device__ __forceinline__ int dma_mn_krow(int i) { return 16 * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
+__device__ __forceinline__ int dma_mn_krow(int i) { return 2 * kDma * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
 __device__ __forceinline__ int dma_mn_piece(int krow) {
   const int l = threadIdx.x & 31;
   return (((l >> 2) ^ (krow & 7)) << 2) | (l & 3);
@@ -211,7 +228,7 @@ struct Acc {
 };
 
 struct Frags {
-  bf16x8 a0, a1, a2, a3, b0, b1, b2, b3;
+  bf16x8 a0, a1, a2, a3, b0, b1, b2, b3;  // a2, a3 unused with 8 waves
 };
 
 // Fragment J of a set (0..3: A blocks, 4..7: B blocks), by compile-time index.
@@ -241,11 +258,9 @@ __device__ __forceinline__ void load_frag(const u32x4* tA, const u32x4* tB, cons
   else frag<J>(g) = frag_at<B_MN, J - 4>(tB, fb, kk);
 }
 
-// Fragment requested r-th (r = 0..7) for a k step: A0, B0, B1, B2, B3, A1,
-// A2, A3.  MFMA j of a step uses A (j >> 2) and B (j & 3), so with reads
-// completing in order the step's first MFMA waits for two reads only, and
-// each later read is needed at least 11 MFMAs after it is issued in the
-// step before.
+// Fragment requested r-th (r < kReads) for a k step: A0, B0, B1, B2, B3, A1
+// (, A2, A3).  MFMA j of a step uses A (j >> 2) and B (j & 3), so with reads
+// completing in order the step's first MFMA waits for two reads only.
 __device__ __forceinline__ constexpr int read_frag(int r) { return r == 0 ? 0 : (r <= 4 ? r + 3 : r - 4); }
 
 template <bool A_MN, bool B_MN>
@@ -257,8 +272,10 @@ __device__ __forceinline__ void load_frags(const u32x4* tA, const u32x4* tB, con
   load_frag<A_MN, B_MN, read_frag(3)>(tA, tB, fa, fb, kk, g);
   load_frag<A_MN, B_MN, read_frag(4)>(tA, tB, fa, fb, kk, g);
   load_frag<A_MN, B_MN, read_frag(5)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(6)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(7)>(tA, tB, fa, fb, kk, g);
+  if constexpr (kReads == 8) {
+    load_frag<A_MN, B_MN, read_frag(6)>(tA, tB, fa, fb, kk, g);
+    load_frag<A_MN, B_MN, read_frag(7)>(tA, tB, fa, fb, kk, g);
+  }
 }
 
 // MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3).
@@ -268,36 +285,46 @@ __device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
   acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
 }
 
-// Wait until at most n (0 or 8) of this thread's vector memory operations
+// Wait until at most n (0 or kDma) of this thread's vector memory operations
 // are outstanding (they complete in issue order, so everything older has
 // landed).
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= kDma) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (n >= kDma) {
+    if constexpr (kDma == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
-static_assert(kDma == 8, "wait_vm counts assume 8 direct loads per operand tile");
+// ... at most 2 kDma (the prologue's second k-block)
+__device__ __forceinline__ void wait_vm_two_tiles() {
+  if constexpr (kDma == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+static_assert(kDma == 8 || kDma == 4, "wait_vm counts assume 8 or 4 direct loads per operand tile");
 
 // Wait for all of this thread's LDS reads (s_waitcnt lgkmcnt(0) through the
 // builtin, which the compiler's own wait insertion takes into account).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// What a k step does besides its 16 MFMAs on f.
+// What a k step does besides its kMma MFMAs on f (16 with 4 waves, 8 with 8).
 enum StepKind {
-  kStepRead,   // request the next step's fragments (g: k step kk of tiles tA, tB), one per two
-               // MFMAs; with kDmaB also direct loads 4 kB0 .. 4 kB0 + 3 of a B tile (lb, k-block
-               // kb, wave slot base dB), one per four MFMAs
-  kStepSwap,   // last step of a k-block: 8 MFMAs; wait until the next k-block has landed and
-               // this wave's reads are done; barrier; then per MFMA one fragment of the next
-               // block's first step (g from tA, tB) and one direct load of an A tile (la, k-block
-               // kb, wave slot base dA)
+  kStepRead,   // request the next step's fragments (g: k step kk of tiles tA, tB): with 4 waves
+               // one per two MFMAs, with 8 one per MFMA from the first; with kDmaB also direct
+               // loads kDma/2 kB0 .. of a B tile (lb, k-block kb, wave slot base dB), one per
+               // four MFMAs
+  kStepSwap,   // last step of a k-block: kMma/2 MFMAs; wait until the next k-block has landed
+               // and this wave's reads are done; barrier; then the next block's first-step
+               // fragments (g from tA, tB: one per MFMA with 4 waves, two with 8) and one direct
+               // load of an A tile per MFMA (la, k-block kb, wave slot base dA)
   kStepLast,   // MFMAs only
 };
 
 // One k step.  No LDS wait is written for the fragment reads: before each
 // MFMA the compiler waits for exactly the reads it needs (LDS reads
-// complete in order).  In a kStepSwap step the barrier sits after the 8th
-// MFMA: by then every fragment of the block has long been read, so the
-// wait before it is short, and after it no wave reads the block's tiles.
+// complete in order).  In a kStepSwap step the barrier sits halfway: by
+// then every fragment of the block has long been read, so the wait before
+// it is short, and after it no wave reads the block's tiles.
 // Bare s_barrier: __syncthreads() would add a release fence that waits for
 // all outstanding loads.  Direct loads are spread one per one to four MFMAs
 // so that the address path never backs up into the wave's in-order issue.
@@ -306,23 +333,35 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
                                       const FragOffs& fa, const FragOffs& fb, int kk, const LA& la, const LB& lb,
                                       int kb, uint32_t dA, uint32_t dB) {
 #define RLK_STEP(J)                                                                              \
-  if constexpr (kKind == kStepRead && (J) % 2 == 0) {                                            \
-    load_frag<A_MN, B_MN, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                            \
-  } else if constexpr (kKind == kStepRead && kDmaB && (J) % 4 == 1) {                            \
-    lb.one(4 * kB0 + (J) / 4, kb, dB);                                                           \
-  } else if constexpr (kKind == kStepSwap && (J) == 8) {                                         \
-    wait_vm(kDma);                                                                               \
-    wait_lds();                                                                                  \
-    __builtin_amdgcn_s_barrier();                                                                \
+  if constexpr ((J) < kMma) {                                                                    \
+    constexpr int kHalf = kMma / 2;                                                              \
+    if constexpr (kKind == kStepRead && kReads == 8 && (J) % 2 == 0) {                           \
+      load_frag<A_MN, B_MN, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                          \
+    } else if constexpr (kKind == kStepRead && kReads == 6 && (J) < 6) {                         \
+      load_frag<A_MN, B_MN, read_frag(J)>(tA, tB, fa, fb, kk, g);                                \
+    }                                                                                            \
+    if constexpr (kKind == kStepRead && kDmaB && (J) % 4 == 1) {                                 \
+      lb.one(kDma / 2 * kB0 + (J) / 4, kb, dB);                                                  \
+    } else if constexpr (kKind == kStepSwap && (J) == kHalf) {                                   \
+      wait_vm(kDma);                                                                             \
+      wait_lds();                                                                                \
+      __builtin_amdgcn_s_barrier();                                                              \
+      __builtin_amdgcn_sched_barrier(0);                                                         \
+    }                                                                                            \
+    if constexpr (kKind == kStepSwap && (J) >= kHalf) {                                          \
+      if constexpr (kReads == 8) {                                                               \
+        load_frag<A_MN, B_MN, read_frag((J) - kHalf)>(tA, tB, fa, fb, 0, g);                     \
+      } else if constexpr (2 * ((J) - kHalf) < kReads) {                                         \
+        load_frag<A_MN, B_MN, read_frag(2 * ((J) - kHalf))>(tA, tB, fa, fb, 0, g);               \
+        load_frag<A_MN, B_MN, read_frag(2 * ((J) - kHalf) + 1)>(tA, tB, fa, fb, 0, g);           \
+      }                                                                                          \
+      la.one((J) - kHalf, kb, dA);                                                               \
+    }                                                                                            \
+    mma1<J>(f, acc);                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-  }                                                                                              \
-  if constexpr (kKind == kStepSwap && (J) >= 8) {                                                \
-    load_frag<A_MN, B_MN, read_frag((J) - 8)>(tA, tB, fa, fb, 0, g);                             \
-    la.one((J) - 8, kb, dA);                                                                     \
-  }                                                                                              \
-  mma1<J>(f, acc);                                                                               \
-  __builtin_amdgcn_sched_barrier(0);
-  static_assert(kDma == 8, "one direct load per MFMA in the second half of a swap step");
+  }
+  static_assert(kDma == kMma / 2, "one direct load per MFMA in the second half of a swap step");
+  static_assert(kDma == 2 * (kMma / 4), "the B tile's loads spread over two read steps");
   __builtin_amdgcn_sched_barrier(0);
   RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
   RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
@@ -346,7 +385,7 @@ template <bool A_MN, bool B_MN, class LA, class LB>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ra0 = 128 * (w & 1), rb0 = 128 * (w >> 1);
+  const int ra0 = kWaveRows * wave_m(w), rb0 = 128 * wave_n(w);
   static_assert(kKK == 4 && kSlots == 5, "schedule written for four k steps and five tile slots");
   // direct-load slot base of this wave in slot 0; slot s is kTileB * s further
   const uint32_t m0s = dma_wave_base(lds_addr(lds));
@@ -357,7 +396,7 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
   const int k1 = min(1, nk - 1);
   lb.dma(k1, m0s + 2 * kTileB);
   la.dma(k1, m0s + 3 * kTileB);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // B0 and A0 have landed
+  wait_vm_two_tiles();  // B0 and A0 have landed
   __builtin_amdgcn_s_barrier();
   const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
   Frags f, g;
@@ -408,7 +447,7 @@ __device__ __forceinline__ void acc_zero(Acc& acc) {
 }
 
 // Tile-local row held by lane l in block mi of wave (wm, *).
-__device__ __forceinline__ int acc_row(int wm, int mi, int lane) { return 128 * wm + 32 * mi + (lane & 31); }
+__device__ __forceinline__ int acc_row(int wm, int mi, int lane) { return kWaveRows * wm + 32 * mi + (lane & 31); }
 
 // Tile-local column of elements 4g .. 4g+3 (first of four) of block ni for
 // lane l in wave (*, wn).

@@ -162,7 +162,7 @@ struct FwdArgs {
 // kSave: also store every active row's fp32 logits (the values the chunk
 // statistics are taken from) for a backward without recompute.
 template <bool kSave>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_tiles(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void fwd_tiles(FwdArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   // tiles: the active-row tiles x every 256-column tile of the range (the
   // count goes through a scalar register: tile addresses derive from it)
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (c0 >= send) return;
   const int c1 = min(c0 + kBN, send);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w), hh = lane >> 5;
   // targets of this lane's rows, loaded ahead of the main loop
   int tgt[kMI];
 #pragma unroll
@@ -404,7 +404,7 @@ struct DzArgs {
 // forward): p = exp(z - lse_i), dz = g_i * ([v == y_i] - p) in fp32, rounded
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
 // are written as zeros.  Each lane stores four consecutive columns (8 bytes).
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dz_tiles(DzArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void dz_tiles(DzArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*a.n_act);
   const int rtiles = (n_act + kBM - 1) / kBM;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));  // columns of this split
   const int c0 = sbeg + j * kBN;
   const int c1 = sbeg + min(j * kBN + kBN, valid_s);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   float4 ri[kMI];  // this lane's rows, loaded ahead of the main loop
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, lane)];
@@ -431,10 +431,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
-  // this wave's 128 rows all active and 128 columns all inside the split
+  // this wave's rows all active and 128 columns all inside the split
   // (wave-uniform; false only on the last row tile and last column tile)
   const int wc0 = j * kBN + 128 * wn;  // first column of the wave within the split
-  const bool full = i0 + 128 * wm + 128 <= n_act && wc0 + 128 <= valid_s;
+  const bool full = i0 + kWaveRows * wm + kWaveRows <= n_act && wc0 + 128 <= valid_s;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
     const int i = i0 + acc_row(wm, mi, lane);
@@ -607,7 +607,7 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
   Acc acc;
   acc_zero(acc);
   gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
-  const int lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  const int lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   float* out = a.grad_W + (size_t)sbeg * a.H;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
@@ -649,7 +649,7 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
   int rt, nt;
   grouped_tile(id, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
   const int i0 = rt * kBM, n0 = nt * kBN;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   int dst[kMI];  // output rows of this lane's active rows, loaded ahead
   if (kLast) {
 #pragma unroll
@@ -716,7 +716,7 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 // then all of them as the grad_h tiles finish.  Either part is skipped when
 // its output pointer is NULL.
 template <bool kFirst, bool kLast>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_tiles(GradHArgs ha,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void grad_tiles(GradHArgs ha,
                                                                                                GradWArgs wa) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*ha.n_act);
@@ -831,7 +831,7 @@ struct GemmArgs {
   void* C;
 };
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tiles(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void gemm_tiles(GemmArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.rtiles * a.ctiles, blockIdx.x);
   if (id < 0) return;
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   Acc acc;
   acc_zero(acc);
   gemm256<false, false>(LA, LB, a.K / kBK, acc, lds);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
     const int i = m0 + acc_row(wm, mi, lane);
