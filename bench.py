@@ -45,7 +45,18 @@ WORKLOADS = {
                               "(rlk_lse_partial x 2 + rlk_lse_merge), Qwen3-8B-shaped LM head"),
     "qwen3_30b_a3b_fwd_bwd": (16384, 2048, 151936, 0.15, True,
                               "linear_logp fwd+bwd, Qwen3-30B-A3B-shaped LM head (T=16384, H=2048, V=151936, 15% rows ignored)"),
+    "qwen3_30b_a3b_tp2_share_fwd_bwd": (6827, 2048, 75968, 0.15, True,
+                                        "linear_logp fwd+bwd at one GPU's share of a tensor-parallel (2-way) "
+                                        "Qwen3-30B-A3B step: T=6827, H=2048, V=75968 (half the vocabulary), "
+                                        "15% rows ignored"),
 }
+
+# Ragged re-batching of the Qwen3-8B-shaped forward: one step = the forward
+# of each batch of rows drawn by synth.rebatch_plan, in its shuffled order.
+REBATCH_WORKLOAD = "qwen3_8b_rebatch_fwd"
+REBATCH_DESC = ("linear_logp fwd over ragged re-batchings of the Qwen3-8B-shaped rows (batches of 1, 7, 128, "
+                "1000 and 8192 rows drawn from seeded permutations of the 4096, in shuffled order; H=4096, "
+                "V=151936, 15% rows ignored)")
 
 # Dense-product workloads (rlk_gemm_bf16_nt): name -> (M, N, K, description).
 GEMM_WORKLOADS = {
@@ -273,6 +284,90 @@ def gemm_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def rebatch_bench(args):
+    """Times the forward over the ragged batches of synth.rebatch_plan: one
+    step runs every batch once (rows gathered ahead, resident in HBM);
+    reports rows/s over the step and the median latency per batch size."""
+    import numpy as np
+    import torch
+
+    import selected_token_lm_amd as rlk
+    import synth
+
+    T, H, V, mask = synth.CONFIGS["qwen3_8b"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(T, H, V, mask)
+    h = torch.from_numpy(inp.h.view(np.int16)).view(torch.bfloat16).to(dev)
+    W = torch.from_numpy(inp.W.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.from_numpy(inp.y).to(dev)
+    plan = synth.rebatch_plan(T)
+    batches = []
+    for rows in plan:
+        r = torch.from_numpy(rows).to(dev)
+        hb, yb = h.index_select(0, r).contiguous(), y.index_select(0, r).contiguous()
+        ws = torch.empty(rlk.workspace_bytes(rlk.OP_FWD, len(rows), H, V), dtype=torch.uint8, device=dev)
+        batches.append((len(rows), int((inp.y[rows] != -100).sum()), hb, yb, ws))
+    rows_step = sum(b[0] for b in batches)
+    act_step = sum(b[1] for b in batches)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(batches) + 1)] for _ in range(args.steps)]
+
+    def step(k=None):
+        for j, (_, _, hb, yb, ws) in enumerate(batches):
+            if k is not None:
+                ev[k][j].record(stream)
+            rlk.linear_logp_fwd(hb, W, yb, ws=ws)
+        if k is not None:
+            ev[k][len(batches)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    rlk.profile_begin()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = rlk.profile_end()
+    ms_ev = sum(ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)) / args.steps
+    ms = max(ms_ev, (t1 - t0) * 1e3 / args.steps)
+    lat = {}
+    for j, b in enumerate(batches):
+        v = sorted(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(args.steps))
+        lat[str(b[0])] = {"active_rows": b[1], "median_ms": v[len(v) // 2], "min_ms": v[0]}
+    n, tot = kern["fwd_tiles"]
+    k_ms = tot / n
+    fl = 2.0 * act_step * H * V / (n / args.steps)  # algorithmic FLOPs per fwd_tiles launch, averaged
+    out = {
+        "metric": f"{args.workload}: tokens/s",
+        "value": rows_step / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": REBATCH_DESC, "rows_per_step": rows_step, "active_rows_per_step": act_step,
+                   "H": H, "V": V, "batches": [b[0] for b in batches], "parallelism": "single GPU"},
+        "batch_latency_ms": lat,
+        "mfma_frac_step": 2.0 * act_step * H * V / (ms * 1e-3) / PEAK_BF16,
+        "roofline": {"bound": "mfma", "kernel": "fwd_tiles", "achieved": fl / (k_ms * 1e-3) / 1e12,
+                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": fl / (k_ms * 1e-3) / PEAK_BF16,
+                     "traffic": None, "flops_per_launch": fl, "avg_launch_ms": k_ms},
+        "kernels": {name: {"launches_per_step": c / args.steps, "avg_ms": t / c} for name, (c, t) in kern.items()},
+        "kernel_digest": kernel_digest("fwd_tiles"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, rows, backward):
     import numpy as np
     import oracle
@@ -305,7 +400,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_8b_fwd_bwd", choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS))
+    ap.add_argument("--workload", default="qwen3_8b_fwd_bwd",
+                    choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS) + [REBATCH_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -331,6 +427,9 @@ def main():
 
     if args.workload in GEMM_WORKLOADS:
         gemm_bench(args)
+        return
+    if args.workload == REBATCH_WORKLOAD:
+        rebatch_bench(args)
         return
 
     T, H, V, mask, do_bwd, desc = WORKLOADS[args.workload]

@@ -309,10 +309,17 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   fa.zsave = zsave;
   fa.ldzs = ldzs;
   fa.zs_spad = (int)ceil_div(g.S, 64) * 64;
-  if (zsave)
-    RLK_LAUNCH_FN("fwd_tiles", rlk::fwd_tiles<true>, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
-  else
-    RLK_LAUNCH_FN("fwd_tiles", rlk::fwd_tiles<false>, dim3((unsigned)fwd_blocks), dim3(rlk::kThreads), st, fa);
+  // batches of at most 96 rows: one row tile whose rows >= 32 * skinny are
+  // padding (the same bits, less work; see gemm_kk).  Not for 97..128 rows:
+  // there the first wave row does all its MFMAs anyway, and merging the
+  // full accumulator set across the per-wave engine copies spills.
+  const int skinny = (!zsave && rlk::kWaves == 4 && T <= 3 * 32) ? (int)ceil_div(T, 32) : 0;
+  const dim3 grid((unsigned)fwd_blocks), block(rlk::kThreads);
+  if (zsave) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<true, 0>), grid, block, st, fa);
+  else if (skinny == 1) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 1>), grid, block, st, fa);
+  else if (skinny == 2) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 2>), grid, block, st, fa);
+  else if (skinny == 3) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 3>), grid, block, st, fa);
+  else RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 0>), grid, block, st, fa);
 
   RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
              nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);

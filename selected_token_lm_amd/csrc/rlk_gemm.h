@@ -263,26 +263,42 @@ __device__ __forceinline__ void load_frag(const u32x4* tA, const u32x4* tB, cons
 // completing in order the step's first MFMA waits for two reads only.
 __device__ __forceinline__ constexpr int read_frag(int r) { return r == 0 ? 0 : (r <= 4 ? r + 3 : r - 4); }
 
-template <bool A_MN, bool B_MN>
+// Row blocks: a wave may compute only its first kRB row blocks (kRB < kMI
+// when the tile's remaining rows are known to be padding); the fragments
+// and MFMAs of the others are skipped.  Fragment J (J < 4: A block J, else
+// B block J - 4) is needed iff this holds.
+template <int kRB>
+__device__ __forceinline__ constexpr bool frag_used(int J) { return J < 4 ? J < kRB : kRB > 0; }
+
+// Fragment J of k step kk if the wave uses it.
+template <bool A_MN, bool B_MN, int kRB, int J>
+__device__ __forceinline__ void load_frag_if(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
+                                             int kk, Frags& g) {
+  if constexpr (frag_used<kRB>(J)) load_frag<A_MN, B_MN, J>(tA, tB, fa, fb, kk, g);
+}
+
+template <bool A_MN, bool B_MN, int kRB = kMI>
 __device__ __forceinline__ void load_frags(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
                                            int kk, Frags& g) {
-  load_frag<A_MN, B_MN, read_frag(0)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(1)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(2)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(3)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(4)>(tA, tB, fa, fb, kk, g);
-  load_frag<A_MN, B_MN, read_frag(5)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(0)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(1)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(2)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(3)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(4)>(tA, tB, fa, fb, kk, g);
+  load_frag_if<A_MN, B_MN, kRB, read_frag(5)>(tA, tB, fa, fb, kk, g);
   if constexpr (kReads == 8) {
-    load_frag<A_MN, B_MN, read_frag(6)>(tA, tB, fa, fb, kk, g);
-    load_frag<A_MN, B_MN, read_frag(7)>(tA, tB, fa, fb, kk, g);
+    load_frag_if<A_MN, B_MN, kRB, read_frag(6)>(tA, tB, fa, fb, kk, g);
+    load_frag_if<A_MN, B_MN, kRB, read_frag(7)>(tA, tB, fa, fb, kk, g);
   }
 }
 
-// MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3).
-template <int J>
+// MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3); skipped for row
+// blocks mi >= kRB.
+template <int J, int kRB = kMI>
 __device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
   constexpr int mi = J >> 2, ni = J & 3;
-  acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
+  if constexpr (mi < kRB)
+    acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
 }
 
 // Wait until at most n (0 or kDma) of this thread's vector memory operations
@@ -328,7 +344,8 @@ enum StepKind {
 // Bare s_barrier: __syncthreads() would add a release fence that waits for
 // all outstanding loads.  Direct loads are spread one per one to four MFMAs
 // so that the address path never backs up into the wave's in-order issue.
-template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB = false, int kB0 = 0, class LA, class LB>
+template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB = false, int kB0 = 0, int kRB = kMI, bool kLoadA = true,
+          class LA, class LB>
 __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* tA, const u32x4* tB,
                                       const FragOffs& fa, const FragOffs& fb, int kk, const LA& la, const LB& lb,
                                       int kb, uint32_t dA, uint32_t dB) {
@@ -336,9 +353,9 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
   if constexpr ((J) < kMma) {                                                                    \
     constexpr int kHalf = kMma / 2;                                                              \
     if constexpr (kKind == kStepRead && kReads == 8 && (J) % 2 == 0) {                           \
-      load_frag<A_MN, B_MN, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                          \
+      load_frag_if<A_MN, B_MN, kRB, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                  \
     } else if constexpr (kKind == kStepRead && kReads == 6 && (J) < 6) {                         \
-      load_frag<A_MN, B_MN, read_frag(J)>(tA, tB, fa, fb, kk, g);                                \
+      load_frag_if<A_MN, B_MN, kRB, read_frag(J)>(tA, tB, fa, fb, kk, g);                        \
     }                                                                                            \
     if constexpr (kKind == kStepRead && kDmaB && (J) % 4 == 1) {                                 \
       lb.one(kDma / 2 * kB0 + (J) / 4, kb, dB);                                                  \
@@ -350,14 +367,14 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
     }                                                                                            \
     if constexpr (kKind == kStepSwap && (J) >= kHalf) {                                          \
       if constexpr (kReads == 8) {                                                               \
-        load_frag<A_MN, B_MN, read_frag((J) - kHalf)>(tA, tB, fa, fb, 0, g);                     \
+        load_frag_if<A_MN, B_MN, kRB, read_frag((J) - kHalf)>(tA, tB, fa, fb, 0, g);             \
       } else if constexpr (2 * ((J) - kHalf) < kReads) {                                         \
-        load_frag<A_MN, B_MN, read_frag(2 * ((J) - kHalf))>(tA, tB, fa, fb, 0, g);               \
-        load_frag<A_MN, B_MN, read_frag(2 * ((J) - kHalf) + 1)>(tA, tB, fa, fb, 0, g);           \
+        load_frag_if<A_MN, B_MN, kRB, read_frag(2 * ((J) - kHalf))>(tA, tB, fa, fb, 0, g);       \
+        load_frag_if<A_MN, B_MN, kRB, read_frag(2 * ((J) - kHalf) + 1)>(tA, tB, fa, fb, 0, g);   \
       }                                                                                          \
-      la.one((J) - kHalf, kb, dA);                                                               \
+      if constexpr (kLoadA) la.one((J) - kHalf, kb, dA);                                         \
     }                                                                                            \
-    mma1<J>(f, acc);                                                                             \
+    mma1<J, kRB>(f, acc);                                                                        \
     __builtin_amdgcn_sched_barrier(0);                                                           \
   }
   static_assert(kDma == kMma / 2, "one direct load per MFMA in the second half of a swap step");
@@ -381,7 +398,13 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
 // so B tiles are issued about 1.5 blocks and A tiles 1 block before use.
 // Loads past the last block repeat the last block's tile into the free slot
 // (uniform load counts; nothing reads that copy); all have landed on return.
-template <bool A_MN, bool B_MN, class LA, class LB>
+//
+// kRB < kMI: this wave computes only its first kRB row blocks (the others
+// are padding rows of the tile).  kLoadA = false: this wave issues none of
+// its A-tile loads (the rows they cover are padding for every wave); B
+// loads, barriers and waits are the same for every wave, so waves with
+// different (kRB, kLoadA) run together in one tile.
+template <bool A_MN, bool B_MN, int kRB = kMI, bool kLoadA = true, class LA, class LB>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
   if (nk <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -392,16 +415,18 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
   constexpr uint32_t kTileB = 16u * kTileU4;
   // prologue: B0, A0 (slots 0, 1), then B1, A1 (slots 2, 3)
   lb.dma(0, m0s);
-  la.dma(0, m0s + kTileB);
+  if constexpr (kLoadA) la.dma(0, m0s + kTileB);
   const int k1 = min(1, nk - 1);
   lb.dma(k1, m0s + 2 * kTileB);
-  la.dma(k1, m0s + 3 * kTileB);
-  wait_vm_two_tiles();  // B0 and A0 have landed
+  if constexpr (kLoadA) la.dma(k1, m0s + 3 * kTileB);
+  // B0 and A0 have landed (block 1's loads may still be in flight)
+  if constexpr (kLoadA) wait_vm_two_tiles();
+  else wait_vm(kDma);
   __builtin_amdgcn_s_barrier();
   const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
   Frags f, g;
   int sb = 0;  // slot of B of the current block (A is in slot sb + 1 mod 5)
-  load_frags<A_MN, B_MN>(lds + kTileU4, lds, fa, fb, 0, f);
+  load_frags<A_MN, B_MN, kRB>(lds + kTileU4, lds, fa, fb, 0, f);
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int sa = sb == 4 ? 0 : sb + 1;
     const u32x4* tA = lds + sa * kTileU4;
@@ -410,16 +435,18 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
     // slot sb (freed by B of block kt at this block's barrier)
     const int k2 = min(kt + 2, nk - 1);
     const int sb2 = sb == 0 ? 4 : sb - 1;
-    kstep<A_MN, B_MN, kStepRead, true, 0>(f, g, acc, tA, tB, fa, fb, 1, la, lb, k2, 0u, m0s + sb2 * kTileB);
+    kstep<A_MN, B_MN, kStepRead, true, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 1, la, lb, k2, 0u,
+                                                         m0s + sb2 * kTileB);
     f = g;
-    kstep<A_MN, B_MN, kStepRead, true, 1>(f, g, acc, tA, tB, fa, fb, 2, la, lb, k2, 0u, m0s + sb2 * kTileB);
+    kstep<A_MN, B_MN, kStepRead, true, 1, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 2, la, lb, k2, 0u,
+                                                         m0s + sb2 * kTileB);
     f = g;
-    kstep<A_MN, B_MN, kStepRead>(f, g, acc, tA, tB, fa, fb, 3, la, lb, 0, 0u, 0u);
+    kstep<A_MN, B_MN, kStepRead, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 3, la, lb, 0, 0u, 0u);
     f = g;
     const int sbn = sb >= 3 ? sb - 3 : sb + 2;  // slot of B of block kt+1
     const int san = sbn == 4 ? 0 : sbn + 1;
-    kstep<A_MN, B_MN, kStepSwap>(f, g, acc, lds + san * kTileU4, lds + sbn * kTileU4, fa, fb, 0, la, lb, k2,
-                                 m0s + sb * kTileB, 0u);
+    kstep<A_MN, B_MN, kStepSwap, false, 0, kRB, kLoadA>(f, g, acc, lds + san * kTileU4, lds + sbn * kTileU4, fa, fb,
+                                                        0, la, lb, k2, m0s + sb * kTileB, 0u);
     f = g;
     sb = sbn;
   }
@@ -429,10 +456,10 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
     const u32x4* tB = lds + sb * kTileU4;
 #pragma unroll
     for (int kk = 0; kk < kKK - 1; ++kk) {
-      kstep<A_MN, B_MN, kStepRead>(f, g, acc, tA, tB, fa, fb, kk + 1, la, lb, 0, 0u, 0u);
+      kstep<A_MN, B_MN, kStepRead, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, kk + 1, la, lb, 0, 0u, 0u);
       f = g;
     }
-    kstep<A_MN, B_MN, kStepLast>(f, g, acc, tA, tB, fa, fb, 0, la, lb, 0, 0u, 0u);
+    kstep<A_MN, B_MN, kStepLast, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 0, la, lb, 0, 0u, 0u);
   }
   // every load issued has landed and every wave is done with the ring
   wait_vm(0);

@@ -159,9 +159,36 @@ struct FwdArgs {
   int zs_spad;   // S rounded up to 64
 };
 
+// Engine call for a K-mode x K-mode tile.  kSkinny = 1..3 (four-wave
+// layout only): the caller guarantees that every valid row of the tile lies
+// below 32 kSkinny (a batch of at most 96 rows, one row tile), so the
+// waves holding rows 128..255 compute nothing, the others only their first
+// kSkinny row blocks, and only the waves whose load rows (64 w .. 64 w + 63)
+// meet those rows load the A tile.  Every element that is computed is the
+// same MFMA chain as in the full tile.
+template <int kSkinny, class LA, class LB>
+__device__ __forceinline__ void gemm_kk(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
+  if constexpr (kSkinny == 0 || kWaves != 4) {
+    gemm256<false, false>(la, lb, nk, acc, lds);
+  } else {
+    static_assert(kSkinny >= 1 && kSkinny < kMI, "row blocks of the first wave row");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w == 0) {
+      gemm256<false, false, kSkinny, true>(la, lb, nk, acc, lds);
+    } else if (w == 2) {
+      gemm256<false, false, kSkinny, false>(la, lb, nk, acc, lds);
+    } else if (w == 1 && kSkinny >= 3) {
+      gemm256<false, false, 0, true>(la, lb, nk, acc, lds);
+    } else {
+      gemm256<false, false, 0, false>(la, lb, nk, acc, lds);
+    }
+  }
+}
+
 // kSave: also store every active row's fp32 logits (the values the chunk
-// statistics are taken from) for a backward without recompute.
-template <bool kSave>
+// statistics are taken from) for a backward without recompute.  kSkinny:
+// see gemm_kk (a batch of at most 32 kSkinny rows).
+template <bool kSave, int kSkinny>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void fwd_tiles(FwdArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   // tiles: the active-row tiles x every 256-column tile of the range (the
@@ -196,7 +223,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   const RowsK B = rows_k(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
   Acc acc;
   acc_zero(acc);
-  gemm256<false, false>(A, B, a.H / kBK, acc, lds);
+  gemm_kk<kSkinny>(A, B, a.H / kBK, acc, lds);
 
   const int cc0 = c0 + kChunk * wn;  // this wave's chunk
   const int width = min(cc0 + kChunk, c1) - cc0;

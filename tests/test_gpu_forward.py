@@ -199,6 +199,21 @@ def test_batch_composition_invariance_small():
         assert torch.equal(logp, ref[r]) and torch.equal(lse, ref_lse[r]), len(rows)
 
 
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 129])
+def test_small_batches_bitwise_equal_to_large_batch(n):
+    # batches of at most 96 rows run with the idle row blocks switched off;
+    # every row must still get the bits of the same row in a large batch
+    inp = synth.make_inputs(400, 576, 9000, 0.15)
+    h, W, y, _ = dev_inputs(inp)
+    ref, ref_lse = rlk.linear_logp_fwd(h, W, y)
+    rows = np.random.Generator(np.random.PCG64(n)).permutation(inp.T)[:n]
+    r = torch.from_numpy(rows).to(DEV)
+    say(f"[fwd] small batch of {n} rows ({int((inp.y[rows] != -100).sum())} active)")
+    logp, lse = rlk.linear_logp_fwd(h[r].contiguous(), W, y[r].contiguous())
+    assert torch.equal(logp, ref[r]) and torch.equal(lse, ref_lse[r])
+    check_vs_oracle(inp, ref, ref_lse, rows[:8])
+
+
 # --- full-size Qwen3-8B-shaped LM head (T=4096, H=4096, V=151936, 15% masked) ---
 
 @pytest.fixture(scope="module")
