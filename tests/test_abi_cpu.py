@@ -63,6 +63,22 @@ def test_workspace_bytes():
         assert W(*bad) == 0, bad
 
 
+def test_dz_budget_override_is_capped(monkeypatch):
+    # RLK_DZ_BUDGET_MB sets the backward's dz block budget up to 2 GiB; a
+    # larger value acts as 2 GiB (tile offsets stay 32-bit)
+    W = rlk.workspace_bytes
+    shape = (1, 65536, 4096, 151936)  # one split's dz block: 2 * 65536 * 4800 B = 600 MiB
+    monkeypatch.setenv("RLK_DZ_BUDGET_MB", "1024")
+    one = W(*shape)
+    monkeypatch.setenv("RLK_DZ_BUDGET_MB", "2048")
+    two = W(*shape)
+    monkeypatch.setenv("RLK_DZ_BUDGET_MB", "100000")
+    big = W(*shape)
+    assert one < two == big
+    per_split = 2 * 65536 * 4800
+    assert two - one == per_split  # G = 1 -> G = 2
+
+
 def fwd(h=FAKE, W=FAKE, y=FAKE, T=64, H=256, V=4096, logp=FAKE, lse=FAKE, ws=FAKE, nbytes=1 << 40):
     return rlk.lib().rlk_linear_logp_fwd(h, W, y, T, H, V, -100, logp, lse, ws, nbytes, None)
 
