@@ -324,7 +324,7 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   else if (skinny == 3) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 3>), grid, block, st, fa);
   else RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 0>), grid, block, st, fa);
 
-  RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(512), st, rec, (size_t)T, zt, idx, n_act, y, gm,
+  RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(64 * rlk::kMergeWaves), st, rec, (size_t)T, zt, idx, n_act, y, gm,
              nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
   return RLK_OK;
 }

@@ -288,14 +288,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 }
 
 // ---------------------------------------------------------------------------
-// Split fold + tree + epilogue.  grid.x: 64 active rows per block; 8 waves,
-// wave w folds splits w, w+8, ... of the range (chunks left to right), the
+// Split fold + tree + epilogue.  grid.x: 64 active rows per block; 16 waves,
+// wave w folds splits w, w+16 of the range (chunks left to right), the
 // split statistics meet in LDS and one thread per row runs the pairwise
 // tree over the nsplit splits.
 // mode 0 (forward):  logp[t] = (z_t - m) - log s, lse[t] = m + log s
 // mode 1 (partial):  pout[t] = {m, s, owned ? z_t : 0, owned}
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void merge_splits(const float2* __restrict__ rec, size_t rec_stride,
+constexpr int kMergeWaves = 16;  // waves of merge_splits (64 rows per block)
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* __restrict__ rec, size_t rec_stride,
                                                     const float* __restrict__ zt, const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ n_act_p,
                                                     const int32_t* __restrict__ y, SplitGeom gm, int nsplit, int mode,
@@ -306,16 +307,26 @@ __global__ __launch_bounds__(512) void merge_splits(const float2* __restrict__ r
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = blockIdx.x * 64 + lane;
   if (blockIdx.x * 64 >= n_act) return;
-  for (int sl = wave; sl < nsplit; sl += 8) {
+  for (int sl = wave; sl < nsplit; sl += kMergeWaves) {
     MS r = ms_identity();
     if (i < n_act) {
-      for (int j = 0; j < gm.cps; ++j) {
-        const int g = sl * gm.cps + j;
-        int c0, c1;
-        chunk_cols(gm, g, c0, c1);
-        if (c0 >= c1) break;
-        const float2 v = rec[(size_t)g * rec_stride + i];
-        r = ms_combine(r, MS{v.x, v.y});
+      // chunks of the split that hold vocabulary columns (the others carry
+      // no record); their records are loaded kBatch at a time ahead of the
+      // fold, which still takes them left to right
+      int c0, c1;
+      chunk_cols(gm, sl * gm.cps, c0, c1);
+      const int send = min(c0 + gm.S, gm.V);
+      const int nj = send > c0 ? (send - c0 + kChunk - 1) / kChunk : 0;
+      const float2* rp = rec + (size_t)sl * gm.cps * rec_stride + i;
+      constexpr int kBatch = 8;
+      for (int j0 = 0; j0 < nj; j0 += kBatch) {
+        float2 buf[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (j0 + u < nj) buf[u] = rp[(size_t)(j0 + u) * rec_stride];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (j0 + u < nj) r = ms_combine(r, MS{buf[u].x, buf[u].y});
       }
     }
     red[sl][lane] = r;
