@@ -441,7 +441,8 @@ struct DzArgs {
 // dz for the group's splits on 256 x 256 tiles (same tiles and logits as the
 // forward): p = exp(z - lse_i), dz = g_i * ([v == y_i] - p) in fp32, rounded
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
-// are written as zeros.  Each lane stores four consecutive columns (8 bytes).
+// are written as zeros.  The tile is staged in LDS and stored row by row
+// (16 bytes per lane, whole 512-byte rows per instruction pair of lanes).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void dz_tiles(DzArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*a.n_act);
@@ -469,17 +470,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
     gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
+  // The dz values go through LDS (free after the main loop) so that every
+  // global store writes whole rows.  LDS tile: 256 rows x 512 bytes; the
+  // 16-byte unit u of row r sits at r * 512 + 16 (u ^ (r & 31)), so the 32
+  // rows that one store from the accumulators touches fall on different
+  // banks and a row read back is still 512 contiguous bytes of one row.
+  char* stage = reinterpret_cast<char*>(lds);
+  auto put = [&](int r, int c, const float (&d)[4]) {
+    const uint32_t off = 512u * r + 16u * ((c >> 3) ^ (r & 31)) + 8u * ((c >> 2) & 1);
+    *reinterpret_cast<uint2*>(stage + off) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+  };
   // this wave's rows all active and 128 columns all inside the split
   // (wave-uniform; false only on the last row tile and last column tile)
   const int wc0 = j * kBN + 128 * wn;  // first column of the wave within the split
   const bool full = i0 + kWaveRows * wm + kWaveRows <= n_act && wc0 + 128 <= valid_s;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
-    const int i = i0 + acc_row(wm, mi, lane);
-    const bool rvalid = i < n_act;
+    const int r = acc_row(wm, mi, lane);
+    const bool rvalid = i0 + r < n_act;
     const float L = ri[mi].x, gi = ri[mi].y;
     const int yl = __float_as_int(ri[mi].z) - sbeg;  // target column within the split
-    uint16_t* drow = dzs + (size_t)i * a.bg.ldz;
     // does this lane hold its row's target column?  (rare)
     const int tl = yl - wc0;
     const bool hit = tl >= 0 && tl < 128 && ((tl >> 2) & 1) == (lane >> 5);
@@ -490,19 +500,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
+          const int c = acc_col4(wn, ni, q, lane);
           float d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) d[e] = gi * (0.f - rlk_exp(acc.c[mi][ni][4 * q + e] - L));
-          *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+          put(r, c, d);
         }
     } else {
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform
-          const int vl0 = j * kBN + acc_col4(wn, ni, q, lane);
+          if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform; never stored
+          const int c = acc_col4(wn, ni, q, lane);
+          const int vl0 = j * kBN + c;
           float d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -511,8 +522,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
             const float delta = (vl == yl) ? 1.f : 0.f;
             d[e] = (rvalid && vl < valid_s) ? gi * (delta - p) : 0.f;
           }
-          *reinterpret_cast<uint2*>(drow + vl0) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+          put(r, c, d);
         }
+    }
+  }
+  __syncthreads();
+  // wave w stores tile rows kBM / kWaves * w ..: two rows per instruction,
+  // lane l the 16-byte unit l & 31 of row 2 it + (l >> 5); units past the
+  // split's padded width belong to the next split and are not written
+  constexpr int kRowsW = kBM / kWaves;
+  const int u = lane & 31;
+  const int col = j * kBN + 8 * u;  // column within the split
+  if (col < a.bg.S_pad) {
+#pragma unroll
+    for (int it = 0; it < kRowsW / 2; ++it) {
+      const int r = kRowsW * w + 2 * it + (lane >> 5);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 512u * r + 16u * (u ^ (r & 31)));
+      *reinterpret_cast<u32x4*>(dzs + (size_t)(i0 + r) * a.bg.ldz + col) = v;
     }
   }
 }
