@@ -157,9 +157,16 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
-def _counter_means(csv_dir, counter):
-    """Mean of `counter` per dispatch for each kernel (short name) in the
-    rocprofv3 counter-collection CSVs under csv_dir."""
+def _short_name(full):
+    """Kernel name without namespace, template arguments and signature
+    (all template instances of one of the library's kernels share it)."""
+    return full.split("(")[0].split("<")[0].split("::")[-1]
+
+
+def _counter_means(csv_dir, counter, key=_short_name):
+    """Mean of `counter` per dispatch for each kernel, grouped by key(full
+    kernel name), over the rocprofv3 counter-collection CSVs under csv_dir
+    (kernels whose key is None are left out)."""
     import csv
     import glob
     per = {}
@@ -168,13 +175,26 @@ def _counter_means(csv_dir, counter):
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                name = r["Kernel_Name"].split("(")[0].split("<")[0].split("::")[-1]
-                key = (name, r["Dispatch_Id"])
-                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                name = key(r["Kernel_Name"])
+                if name is None:
+                    continue
+                k = (name, r["Dispatch_Id"])
+                per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
     out = {}
     for (name, _), v in per.items():
         out.setdefault(name, []).append(v)
     return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+# The calibration copy: torch.neg over COPY_BYTES (copy_calibration).  Only
+# its own dispatches count: torch's other elementwise kernels (the fill that
+# creates the source, for one) share its short name and move other byte
+# counts.
+CALIBRATION_KERNEL = "neg_kernel"
+
+
+def _calibration_key(full):
+    return "copy" if CALIBRATION_KERNEL in full else None
 
 
 def traffic_from(run_dir, command):
@@ -185,19 +205,36 @@ def traffic_from(run_dir, command):
     what it reads for the calibration copy (COPY_BYTES each way)."""
     fetch = _counter_means(os.path.join(run_dir, "fetch"), "FETCH_SIZE")
     write = _counter_means(os.path.join(run_dir, "write"), "WRITE_SIZE")
-    copy = [k for k in fetch if "elementwise" in k or "neg" in k.lower()]
-    if not copy:
-        raise SystemExit(f"no calibration copy kernel among {sorted(fetch)}")
-    ck = copy[0]
-    f_scale = COPY_BYTES / (fetch[ck][0] * 1024.0)
-    w_scale = COPY_BYTES / (write[ck][0] * 1024.0)
+    # the machine code the counters were taken on: the JSON line each
+    # counter run printed (run_dir/fetch.log, run_dir/write.log)
+    measured = []
+    for log in ("fetch.log", "write.log"):
+        with open(os.path.join(run_dir, log)) as f:
+            lines = [ln for ln in f if ln.startswith("{")]
+        if not lines:
+            raise SystemExit(f"no bench JSON line in {os.path.join(run_dir, log)}")
+        measured.append(json.loads(lines[-1]).get("kernel_digests", {}))
+    if measured[0] != measured[1]:
+        raise SystemExit("the FETCH_SIZE and WRITE_SIZE runs measured different builds")
+    f_copy = _counter_means(os.path.join(run_dir, "fetch"), "FETCH_SIZE", _calibration_key)
+    w_copy = _counter_means(os.path.join(run_dir, "write"), "WRITE_SIZE", _calibration_key)
+    if "copy" not in f_copy or "copy" not in w_copy:
+        raise SystemExit(f"no dispatch of the calibration copy ({CALIBRATION_KERNEL}) under {run_dir}")
+    ck = f"torch.neg over {COPY_BYTES} bytes ({CALIBRATION_KERNEL}, {f_copy['copy'][1]} dispatches)"
+    f_scale = COPY_BYTES / (f_copy["copy"][0] * 1024.0)
+    w_scale = COPY_BYTES / (w_copy["copy"][0] * 1024.0)
     rows = []
     for k in GEMM_KERNELS:
         if k not in fetch or k not in write:
             continue
         fb = fetch[k][0] * 1024.0 * f_scale
         wb = write[k][0] * 1024.0 * w_scale
-        rec = {"kernel": k, "kernel_digest": kernel_digest(k), "bytes_per_launch": fb + wb, "fetch_bytes": fb,
+        if k not in measured[0]:
+            continue
+        if measured[0][k] != kernel_digest(k):
+            print(f"{k}: the library has changed since these counters were taken; the record keeps the "
+                  f"measured digest and bench.py will report no traffic for it", flush=True)
+        rec = {"kernel": k, "kernel_digest": measured[0][k], "bytes_per_launch": fb + wb, "fetch_bytes": fb,
                "write_bytes": wb, "dispatches": fetch[k][1], "calibration_kernel": ck,
                "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
         with open(os.path.join(ROOT, "profiles", f"traffic_{k}.json"), "w") as f:
@@ -561,6 +598,7 @@ def main():
                                + (zsave.numel() * 4 if saved else 0)),
         "peak_reserved_delta_mb": (peak_reserved - reserved0) / 2**20,
         "kernel_digest": kernel_digest(dom),
+        "kernel_digests": {k: kernel_digest(k) for k in GEMM_KERNELS if k in kernels},
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_rows} rows)", file=sys.stderr, flush=True)

@@ -538,7 +538,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
     for (int it = 0; it < kRowsW / 2; ++it) {
       const int r = kRowsW * w + 2 * it + (lane >> 5);
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 512u * r + 16u * (u ^ (r & 31)));
-      *reinterpret_cast<u32x4*>(dzs + (size_t)(i0 + r) * a.bg.ldz + col) = v;
+      // streaming store: dz is read back only by the next launch, so it
+      // should not displace the W and h lines the other tiles still use
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dzs + (size_t)(i0 + r) * a.bg.ldz + col));
     }
   }
 }
