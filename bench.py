@@ -197,8 +197,8 @@ def _calibration_key(full):
     return "copy" if CALIBRATION_KERNEL in full else None
 
 
-def traffic_from(run_dir, command):
-    """Writes profiles/traffic_<kernel>.json for the GEMM kernels from two
+def traffic_from(run_dir, command, out_dir=None):
+    """Writes <out_dir>/traffic_<kernel>.json (default: profiles/) for the GEMM kernels from two
     counter runs of `bench.py --steps 2 --warmup 1 --no-cpu-baseline
     --copy-calibration` (run_dir/fetch: --pmc FETCH_SIZE, run_dir/write:
     --pmc WRITE_SIZE; both in KiB per dispatch).  Each counter is scaled by
@@ -237,7 +237,7 @@ def traffic_from(run_dir, command):
         rec = {"kernel": k, "kernel_digest": measured[0][k], "bytes_per_launch": fb + wb, "fetch_bytes": fb,
                "write_bytes": wb, "dispatches": fetch[k][1], "calibration_kernel": ck,
                "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
-        with open(os.path.join(ROOT, "profiles", f"traffic_{k}.json"), "w") as f:
+        with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{k}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         rows.append(rec)
         print(f"{k}: fetch {fb / 1e9:.3f} GB, write {wb / 1e9:.3f} GB per launch", flush=True)
