@@ -245,10 +245,94 @@ def traffic_from(run_dir, command, out_dir=None):
     return rows
 
 
+class ClockPowerSampler:
+    """GFX clock and socket power of the benchmarked GPU, read through
+    amdsmi on a helper thread every `period` seconds (the firmware refreshes
+    them less often; repeats are kept).  Everything degrades to None where
+    amdsmi is missing or refuses."""
+
+    def __init__(self, torch, period=0.02):
+        import threading
+        self.period, self.samples, self.handle, self.smi = period, [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                    self.handle = h
+        except Exception:  # no amdsmi, no permission: report nothing
+            self.handle = None
+
+    def _read(self):
+        c = self.smi.amdsmi_get_clock_info(self.handle, self.smi.AmdSmiClkType.GFX)
+        p = self.smi.amdsmi_get_power_info(self.handle)
+        return c["clk"], c["max_clk"], p["current_socket_power"], p["power_limit"]
+
+    def _loop(self):
+        while not self._stop.wait(self.period):
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+
+    def start(self):
+        if self.handle is None:
+            return
+        import threading
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self, skip=0):
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        try:
+            self.smi.amdsmi_shut_down()
+        except Exception:
+            pass
+        s = [x for x in self.samples[skip:] if all(isinstance(v, (int, float)) for v in x)]
+        if not s:
+            return None
+        clk = sorted(x[0] for x in s)
+        pw = sorted(x[2] for x in s)
+        return {"gfx_clock_mhz": {"median": clk[len(clk) // 2], "min": clk[0], "max": clk[-1]},
+                "max_gfx_clock_mhz": s[0][1],
+                "socket_power_w": {"median": pw[len(pw) // 2], "max": pw[-1]},
+                "power_limit_w": s[0][3] / 1e6,
+                "samples": len(s)}
+
+
+def clock_power_window(torch, step, seconds=2.5, settle=0.75):
+    """Steady-state GFX clock and socket power under this workload: `step`
+    repeated for `seconds` after the timed region (not part of any timing),
+    sampled by ClockPowerSampler; samples of the first `settle` seconds
+    (clock ramp, firmware refresh) are dropped."""
+    sampler = ClockPowerSampler(torch)
+    if sampler.handle is None:
+        return None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sampler.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    n_settle = int(settle / sampler.period)
+    res = sampler.stop(skip=n_settle)
+    if res is not None:
+        res["source"] = (f"amdsmi every {sampler.period * 1e3:.0f} ms while the step repeats for "
+                         f"{seconds:.1f} s after the timed region (first {settle:.2f} s dropped)")
+    return res
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
-    # the GFX clock under load is not exposed here; profiles/ derives it from
-    # GRBM_GUI_ACTIVE cycles over kernel time
+    # the clock and power under load come from ClockPowerSampler
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count}
 
 
@@ -291,6 +375,8 @@ def gemm_bench(args):
     out_dtype = torch.bfloat16 if args.workload.endswith("_bf16") else torch.float32
     ms = timed(lambda: rlk.gemm_bf16_nt(A, B, out_dtype=out_dtype), args.steps, args.warmup)
     kern = rlk.profile_end()
+    clock_power = None if args.no_clock_power else clock_power_window(
+        torch, lambda: rlk.gemm_bf16_nt(A, B, out_dtype=out_dtype))
     n, tot = kern["gemm_tiles"]
     k_ms = tot / n
     Bt = B.t()
@@ -310,6 +396,7 @@ def gemm_bench(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "N": N, "K": K},
+        "clock_power": clock_power,
         "roofline": {"bound": "mfma", "kernel": "gemm_tiles", "achieved": achieved / 1e12,
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
                      "traffic": traffic_for("gemm_tiles"), "flops_per_launch": flops,
@@ -370,6 +457,7 @@ def rebatch_bench(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = rlk.profile_end()
+    clock_power = None if args.no_clock_power else clock_power_window(torch, step)
     ms_ev = sum(ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)) / args.steps
     ms = max(ms_ev, (t1 - t0) * 1e3 / args.steps)
     lat = {}
@@ -395,6 +483,7 @@ def rebatch_bench(args):
         "config": {"workload": REBATCH_DESC, "rows_per_step": rows_step, "active_rows_per_step": act_step,
                    "H": H, "V": V, "batches": [b[0] for b in batches], "parallelism": "single GPU"},
         "batch_latency_ms": lat,
+        "clock_power": clock_power,
         "mfma_frac_step": 2.0 * act_step * H * V / (ms * 1e-3) / PEAK_BF16,
         "roofline": {"bound": "mfma", "kernel": "fwd_tiles", "achieved": fl / (k_ms * 1e-3) / 1e12,
                      "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": fl / (k_ms * 1e-3) / PEAK_BF16,
@@ -441,6 +530,8 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS) + [REBATCH_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-clock-power", action="store_true",
+                    help="skip the extra steps that sample the GFX clock and socket power (use under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain copies of a known size (HBM counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -531,6 +622,7 @@ def main():
     per_step = sorted(step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps))
     kern = rlk.profile_end()
     peak_reserved = torch.cuda.max_memory_reserved()
+    clock_power = None if args.no_clock_power or args.copy_calibration else clock_power_window(torch, step)
     if args.copy_calibration:
         copy_calibration(dev)
     # the part's MFMA ceiling on this machine right now (pure MFMA, random
@@ -586,10 +678,16 @@ def main():
         "step_ms_median_p10_p90": [per_step[len(per_step) // 2], per_step[len(per_step) // 10],
                                    per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)]],
         "device": device_info(torch),
+        "clock_power": clock_power,
         "mfma_frac_step": flops_step / (ms * 1e-3) / PEAK_BF16,
         "algorithmic_tflop_per_step": flops_step / 1e12,
         "roofline": roofline,
         "kernels": kernels,
+        "peak_at_measured_clock": None if not clock_power else {
+            "what": "the 2.5 PFLOP/s bf16 peak scaled by the median GFX clock under this workload over the "
+                    "2.4 GHz it assumes (clock_power)",
+            "tflops": PEAK_BF16 / 1e12 * clock_power["gfx_clock_mhz"]["median"] / 2400.0,
+            "dominant_kernel_frac": achieved / (PEAK_BF16 * clock_power["gfx_clock_mhz"]["median"] / 2400.0)},
         "mfma_ceiling": {"what": "pure v_mfma_f32_32x32x16_bf16 loop on random bf16 operands, no memory traffic, "
                                  "same box after the timed steps (rlk_bench_mfma_ceiling)",
                          "best_tflops": ceiling["best_tflops"], "median_tflops": ceiling["median_tflops"],
