@@ -659,6 +659,11 @@ def main():
         "flops_per_launch": dom_fl,
         "avg_launch_ms": kernels[dom]["avg_ms"],
     }
+    if roofline["traffic"]:
+        # diagnostic beside the MFMA bound: the dominant kernel's measured HBM
+        # bytes per launch over its launch time, against the HBM3E peak
+        roofline["traffic_gbps"] = roofline["traffic"] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+        roofline["traffic_frac_of_hbm_peak"] = roofline["traffic_gbps"] * 1e9 / PEAK_HBM
 
     out = {
         "metric": METRIC if args.workload == "qwen3_8b_fwd_bwd" else f"{args.workload}: tokens/s",
