@@ -404,9 +404,21 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
 // its A-tile loads (the rows they cover are padding for every wave); B
 // loads, barriers and waits are the same for every wave, so waves with
 // different (kRB, kLoadA) run together in one tile.
-template <bool A_MN, bool B_MN, int kRB = kMI, bool kLoadA = true, class LA, class LB>
-__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
-  if (nk <= 0) return;
+//
+// tail(): run once just before the last k-block's MFMAs, for loads whose
+// values only the caller's epilogue needs (they land under that block's
+// MFMAs and take no registers through the loop; all have landed on return).
+struct NoTail {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <bool A_MN, bool B_MN, int kRB = kMI, bool kLoadA = true, class LA, class LB, class Tail = NoTail>
+__device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds,
+                                        const Tail& tail = Tail{}) {
+  if (nk <= 0) {
+    tail();
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = kWaveRows * wave_m(w), rb0 = 128 * wave_n(w);
   static_assert(kKK == 4 && kSlots == 5, "schedule written for four k steps and five tile slots");
@@ -451,6 +463,7 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
     sb = sbn;
   }
   {
+    tail();
     const int sa = sb == 4 ? 0 : sb + 1;
     const u32x4* tA = lds + sa * kTileU4;
     const u32x4* tB = lds + sb * kTileU4;

@@ -93,16 +93,6 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
   c1 = min(c0 + kChunk, send);
 }
 
-// Element k of a row's 64 values, selected by a per-lane k (a chain of
-// compares and selects; indexing a register array with k would move the
-// array to memory).
-__device__ __forceinline__ float pick64(const float (&v)[64], int k) {
-  float x = 0.f;
-#pragma unroll
-  for (int e = 0; e < 64; ++e) x = (k == e) ? v[e] : x;
-  return x;
-}
-
 // Balanced pairwise tree over e[0..63]: adjacent pairs, then pairs of pairs.
 // (Fixed-size levels: every index is a compile-time constant.)
 __device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
@@ -136,6 +126,23 @@ __device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
 //   s   = T(e of half 0) + T(e of half 1), T = balanced pairwise tree over
 //         the half's 64 columns in ascending order.
 // ---------------------------------------------------------------------------
+// (m, s) of one row of a chunk from this lane's 64 values v and its
+// partner lane's (the other half of the row); columns outside the chunk
+// enter as -inf (they do not move the max, and their e is exp(-inf) = 0).
+__device__ __forceinline__ float2 chunk_stats(const float (&v)[64]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) mx = fmaxf(mx, v[k]);
+  float lo, hi;
+  lane_halves(mx, lo, hi);
+  mx = fmaxf(lo, hi);
+  float e[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) e[k] = rlk_exp(v[k] - mx);
+  lane_halves(tree_sum64(e), lo, hi);
+  return make_float2(mx, lo + hi);
+}
+
 struct TileGeom {
   int tps;  // 256-column tiles per split = ceil(S / 256)
 };
@@ -166,21 +173,21 @@ struct FwdArgs {
 // kSkinny row blocks, and only the waves whose load rows (64 w .. 64 w + 63)
 // meet those rows load the A tile.  Every element that is computed is the
 // same MFMA chain as in the full tile.
-template <int kSkinny, class LA, class LB>
-__device__ __forceinline__ void gemm_kk(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds) {
+template <int kSkinny, class LA, class LB, class Tail>
+__device__ __forceinline__ void gemm_kk(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds, const Tail& tail) {
   if constexpr (kSkinny == 0 || kWaves != 4) {
-    gemm256<false, false>(la, lb, nk, acc, lds);
+    gemm256<false, false>(la, lb, nk, acc, lds, tail);
   } else {
     static_assert(kSkinny >= 1 && kSkinny < kMI, "row blocks of the first wave row");
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w == 0) {
-      gemm256<false, false, kSkinny, true>(la, lb, nk, acc, lds);
+      gemm256<false, false, kSkinny, true>(la, lb, nk, acc, lds, tail);
     } else if (w == 2) {
-      gemm256<false, false, kSkinny, false>(la, lb, nk, acc, lds);
+      gemm256<false, false, kSkinny, false>(la, lb, nk, acc, lds, tail);
     } else if (w == 1 && kSkinny >= 3) {
-      gemm256<false, false, 0, true>(la, lb, nk, acc, lds);
+      gemm256<false, false, 0, true>(la, lb, nk, acc, lds, tail);
     } else {
-      gemm256<false, false, 0, false>(la, lb, nk, acc, lds);
+      gemm256<false, false, 0, false>(la, lb, nk, acc, lds, tail);
     }
   }
 }
@@ -209,21 +216,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   const int c1 = min(c0 + kBN, send);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w), hh = lane >> 5;
-  // targets of this lane's rows, loaded ahead of the main loop
-  int tgt[kMI];
+  // targets (and, kSave, original rows) of this lane's rows: loaded while
+  // the last k-block's MFMAs run, so that nothing of them is kept through
+  // the main loop
+  int tgt[kMI], trow[kMI];
+  const auto load_rows = [&]() {
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi) tgt[mi] = a.yA[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
-  int trow[kMI];  // original rows (kSave only)
-  if (kSave) {
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) trow[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
-  }
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int r = min(i0 + acc_row(wm, mi, lane), n_act - 1);
+      tgt[mi] = a.yA[r];
+      if (kSave) trow[mi] = a.idx[r];
+    }
+  };
 
   const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
   const RowsK B = rows_k(a.W + (size_t)(c0 - a.gm.vocab_start) * a.H, c1 - 1 - c0, a.H);
   Acc acc;
   acc_zero(acc);
-  gemm_kk<kSkinny>(A, B, a.H / kBK, acc, lds);
+  gemm_kk<kSkinny>(A, B, a.H / kBK, acc, lds, load_rows);
 
   const int cc0 = c0 + kChunk * wn;  // this wave's chunk
   const int width = min(cc0 + kChunk, c1) - cc0;
@@ -235,6 +245,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   for (int mi = 0; mi < kMI; ++mi) {
     const int i = i0 + acc_row(wm, mi, lane);
     // the row's 64 values of this lane, out of the accumulator once
+    // one row block at a time: its values leave the accumulators here and
+    // not earlier (the scheduler would otherwise hoist every block's moves)
+    __builtin_amdgcn_sched_barrier(0);
     float v[64];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
@@ -260,30 +273,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
         }
     }
     // target logit: rare (a row's target lies in a given chunk about once in
-    // a thousand), so the select chain runs only when some lane needs it
+    // a thousand).  When some lane of the wave needs one, the wave's values
+    // go through LDS, which is free once the engine has returned: lane l
+    // writes its element k at float4 slot 64 (k >> 2) + l of the wave's
+    // 16 KB and reads back only its own slots.
     const int tc = tgt[mi] - cc0;
     const bool hit = i < n_act && tc >= 0 && tc < width && ((tc >> 2) & 1) == hh;
     if (__builtin_amdgcn_ballot_w64(hit)) {
-      const float z = pick64(v, ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3));
-      if (hit) a.zt[i] = z;
+      float4* sl = reinterpret_cast<float4*>(lds) + 1024 * w;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sl[64 * q + lane] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      if (hit) {
+        const int k = ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3);
+        a.zt[i] = reinterpret_cast<const float*>(sl + 64 * (k >> 2) + lane)[k & 3];
+      }
     }
-    if (width < kChunk) {  // short last chunk of a split (wave-uniform)
+    // the short last chunk of a split (a wave-uniform branch): its missing
+    // columns as -inf, in a copy, so that only (m, s) leaves either branch
+    float2 st;
+    if (width < kChunk) {
+      float u[64];
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) v[16 * ni + r] = -INFINITY;
+          u[16 * ni + r] = 32 * ni + 8 * (r >> 2) + (r & 3) < lim ? v[16 * ni + r] : -INFINITY;
+      st = chunk_stats(u);
+    } else {
+      st = chunk_stats(v);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 64; ++k) mx = fmaxf(mx, v[k]);
-    float lo, hi;
-    lane_halves(mx, lo, hi);
-    mx = fmaxf(lo, hi);
-#pragma unroll
-    for (int k = 0; k < 64; ++k) v[k] = rlk_exp(v[k] - mx);
-    lane_halves(tree_sum64(v), lo, hi);
-    if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = make_float2(mx, lo + hi);
+    if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = st;
   }
 }
 
