@@ -165,12 +165,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 // apart for every read form).  gemm256 orders them explicitly: a slot is
 // read only after wait_vm and a barrier, and refilled only after a barrier
 // that follows the last reads of it.
-// m0: LDS byte address of the instruction's 1 KB (wave-uniform).
+// m0: LDS byte address of the instruction's 1 KB (wave-uniform), bound to
+// the M0 register by the operand constraint, so the compiler sets M0 itself
+// and knows the statement reads it; the s_nop is the one wait state that a
+// write of M0 needs before an LDS-direct load.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(off), "s"(base)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
 // K-mode row and piece of instruction i for this thread
