@@ -13,7 +13,7 @@ import torch
 import oracle
 import selected_token_lm_amd as rlk
 import synth
-from tests.gpu_util import DEV, GRAD_RTOL, config, dev_inputs, rel_l2, say, to64
+from tests.gpu_util import DEV, GRAD_RTOL, config, dev_inputs, rel_l2, say, target_sweep, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,22 @@ def test_small_shapes_match_oracle(T, H, V, mask):
     assert e_h <= GRAD_RTOL and e_W <= GRAD_RTOL
     masked = inp.y == -100
     assert torch.all(gh[torch.from_numpy(masked).to(DEV)] == 0)
+
+
+def test_target_at_every_tile_position():
+    """The delta term of dz lands on the target column at any of a tile's
+    lane / element positions and at the split and vocabulary edges."""
+    inp = target_sweep()
+    say(f"bwd target sweep T={inp.T} H={inp.H} V={inp.V}")
+    _, logp, lse, gh, gW = fwd_bwd(inp)
+    ref_gh, ref_gW = oracle.backward(inp.h, inp.W, inp.y, inp.g)
+    e_h = rel_l2(to64(gh), ref_gh)
+    e_W = rel_l2(to64(gW), ref_gW)
+    # the target columns' rows of grad_W carry the delta terms: each on its own
+    act = inp.y[inp.y >= 0]
+    e_Wy = rel_l2(to64(gW)[act], ref_gW[act])
+    say(f"  relL2 grad_h={e_h:.3e} grad_W={e_W:.3e} target rows of grad_W={e_Wy:.3e}")
+    assert e_h <= GRAD_RTOL and e_W <= GRAD_RTOL and e_Wy <= GRAD_RTOL
 
 
 def test_grad_subsets_and_flags():

@@ -15,7 +15,7 @@ import oracle
 import selected_token_lm_amd as rlk
 import synth
 from tests.gpu_util import (DEV, LOGP_TOL, bf16_dev, config, dev_inputs, f32_minus_log, i32_dev,
-                            say, to64)
+                            say, target_sweep, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,16 @@ def test_tiny_config_matches_oracle():
 def test_ragged_shapes_match_oracle(T, H, V, mask):
     say(f"ragged T={T} H={H} V={V}")
     inp = synth.make_inputs(T, H, V, mask)
+    logp, lse = run_fwd(inp)
+    check_vs_oracle(inp, logp, lse)
+
+
+@pytest.mark.parametrize("rows", [None, 64])
+def test_target_at_every_tile_position(rows):
+    inp = target_sweep()
+    if rows is not None:  # a small batch takes the kernel instance for at most 96 rows
+        inp.h, inp.y, inp.g, inp.T = inp.h[:rows], inp.y[:rows], inp.g[:rows], rows
+    say(f"target sweep T={inp.T} H={inp.H} V={inp.V}")
     logp, lse = run_fwd(inp)
     check_vs_oracle(inp, logp, lse)
 

@@ -14,7 +14,7 @@ import torch
 import selected_token_lm_amd as rlk
 import synth
 from oracle import gemm as og
-from tests.gpu_util import DEV, bf16_dev, config, dev_inputs, say
+from tests.gpu_util import DEV, bf16_dev, config, dev_inputs, say, target_sweep
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,16 @@ def same_bits(a, b):
 @pytest.mark.parametrize("T,H,V,mask", [(64, 256, 4096, 0.0), (300, 192, 5000, 0.2), (37, 64, 1000, 0.3)])
 def test_small_shapes_bitwise_equal_to_recompute(T, H, V, mask):
     say(f"[saved] T={T} H={H} V={V} mask={mask}")
-    inp = synth.make_inputs(T, H, V, mask)
+    check_equal_to_recompute(synth.make_inputs(T, H, V, mask))
+
+
+def test_target_sweep_bitwise_equal_to_recompute():
+    inp = target_sweep()
+    say(f"[saved] target sweep T={inp.T} H={inp.H} V={inp.V}")
+    check_equal_to_recompute(inp)
+
+
+def check_equal_to_recompute(inp):
     h, W, y, g = dev_inputs(inp)
     logp0, lse0 = rlk.linear_logp_fwd(h, W, y)
     logp1, lse1, z = rlk.linear_logp_fwd_save(h, W, y)
