@@ -199,7 +199,13 @@ struct ProfScope {
     if (!g_prof_on) return;
     a = prof_event();
     b = prof_event();
-    if (a && b) (void)hipEventRecord(a, st);
+    if (a && b) {
+      (void)hipEventRecord(a, st);
+    } else {  // event creation failed: this launch goes untimed
+      if (a) g_prof_pool.push_back(a);
+      if (b) g_prof_pool.push_back(b);
+      a = b = nullptr;
+    }
   }
   ~ProfScope() {
     if (!a || !b) return;
