@@ -537,6 +537,9 @@ def main():
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter runs under DIR into profiles/traffic_*.json")
     ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="override the workload's row count T (throughput against batch size; "
+                         "not the headline configuration)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from, args.traffic_command)
@@ -553,6 +556,11 @@ def main():
     import selected_token_lm_amd as rlk
     import synth
 
+    if args.rows is not None and (args.workload in GEMM_WORKLOADS or args.workload == REBATCH_WORKLOAD
+                                  or args.rows < 1):
+        print("--rows takes a positive row count and applies to the linear_logp workloads only",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload in GEMM_WORKLOADS:
         gemm_bench(args)
         return
@@ -561,6 +569,9 @@ def main():
         return
 
     T, H, V, mask, do_bwd, desc = WORKLOADS[args.workload]
+    if args.rows is not None:
+        desc = desc.replace(f"T={T},", f"T={args.rows},") + f" [rows overridden: T={args.rows}]"
+        T = args.rows
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
@@ -666,7 +677,8 @@ def main():
         roofline["traffic_frac_of_hbm_peak"] = roofline["traffic_gbps"] * 1e9 / PEAK_HBM
 
     out = {
-        "metric": METRIC if args.workload == "qwen3_8b_fwd_bwd" else f"{args.workload}: tokens/s",
+        "metric": (METRIC if args.workload == "qwen3_8b_fwd_bwd" and args.rows is None
+                   else f"{args.workload}{'' if args.rows is None else f' at T={T}'}: tokens/s"),
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
