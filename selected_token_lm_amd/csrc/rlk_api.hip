@@ -136,7 +136,8 @@ BwdWs bwd_layout(int64_t T, int64_t H, int64_t V) {
 
 // --- device check ----------------------------------------------------------------
 std::mutex g_dev_mu;
-int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+int g_dev_ok[64];   // 0 unknown, 1 gfx950, -1 other
+int g_dev_cus[64];  // compute units of a checked device
 
 rlk_status check_device() {
   int dev = 0;
@@ -149,10 +150,30 @@ rlk_status check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(RLK_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_cus[dev] = prop.multiProcessorCount;
     if (g_dev_ok[dev] < 0) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
   }
   if (g_dev_ok[dev] < 0) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
   return RLK_OK;
+}
+
+// Compute units of the current device (after check_device succeeded on it).
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  return g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
+}
+
+// grad_h in row passes (gradh_tile's kPart) when its full tiles fit on the
+// compute units kMI times over, i.e. when each would otherwise run the
+// vocabulary-long chain alone while most units idle.  The environment
+// variable RLK_GRAD_H_PASSES = 0 / 1 forces either form (results are the
+// same bits; tests use it).
+bool grad_h_passes(int64_t row_tiles, int64_t n_tiles) {
+  const char* e = std::getenv("RLK_GRAD_H_PASSES");
+  if (e && *e) return std::atoi(e) != 0;
+  return (int64_t)rlk::kMI * row_tiles * n_tiles <= device_cus();
 }
 
 // Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension.
@@ -468,7 +489,8 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
   const int G = (int)L.G;
   // grids: every row tile of T (the kernels keep those of active rows)
   const int64_t dz_blocks = 8 * ceil_div(row_tiles * G * tps, 8);
-  const int64_t gh_blocks = grad_h ? 8 * ceil_div(row_tiles * n_tiles, 8) : 0;
+  const bool passes = grad_h && grad_h_passes(row_tiles, n_tiles);
+  const int64_t gh_blocks = grad_h ? 8 * ceil_div(row_tiles * n_tiles * (passes ? rlk::kMI : 1), 8) : 0;
   const int64_t gw_blocks = grad_W ? 8 * ceil_div((int64_t)n_tiles * G * tps, 8) : 0;
   RLK_TRY(check_grid(dz_blocks));
   RLK_TRY(check_grid(gh_blocks + gw_blocks));
@@ -519,8 +541,10 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
     ha.grad_h = static_cast<uint16_t*>(grad_h);
     const bool first = c_lo == 0, last = c_lo + G > last_split;
     void (*kfn)(rlk::GradHArgs, rlk::GradWArgs) =
-        first ? (last ? rlk::grad_tiles<true, true> : rlk::grad_tiles<true, false>)
-              : (last ? rlk::grad_tiles<false, true> : rlk::grad_tiles<false, false>);
+        passes ? (first ? (last ? rlk::grad_tiles<true, true, true> : rlk::grad_tiles<true, false, true>)
+                        : (last ? rlk::grad_tiles<false, true, true> : rlk::grad_tiles<false, false, true>))
+               : (first ? (last ? rlk::grad_tiles<true, true, false> : rlk::grad_tiles<true, false, false>)
+                        : (last ? rlk::grad_tiles<false, true, false> : rlk::grad_tiles<false, false, false>));
     RLK_LAUNCH_FN("grad_tiles", kfn, dim3((unsigned)(gh_blocks + gw_blocks)), dim3(rlk::kThreads), st, ha, wa);
   }
   return ok();

@@ -729,16 +729,28 @@ struct GradHArgs {
 // the last group it is rounded to bf16 once and written to the row's place.
 // kFirst / kLast: the group is the first / last one (compile-time, so that
 // the accumulators never merge across a branch).  Tile id: (row tile, H tile).
-template <bool kFirst, bool kLast>
+//
+// kPart: the tile's rows in kMI passes, id = kMI * tile + p.  Pass p reads
+// the dz tile from 32 p rows further down and every wave computes only its
+// first 32-row block, i.e. tile rows 32 p + kWaveRows wm + 0..31 (the
+// passes cover all of them); only the waves whose load rows meet those
+// rows load the dz tile.  kMI times the workgroups, each with 1 / kMI of
+// the MFMAs per k-block: for batches whose few grad_h tiles would each run
+// the vocabulary-long chain on a compute unit of their own while the
+// others idle.  Every element is the same MFMA chain as in a full tile.
+template <bool kFirst, bool kLast, bool kPart>
 __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int n_act, u32x4* lds) {
+  constexpr int kPasses = kPart ? kMI : 1;
+  constexpr int kBlocks = kPart ? 1 : kMI;  // row blocks per wave
+  const int pass = id % kPasses;
   int rt, nt;
-  grouped_tile(id, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
-  const int i0 = rt * kBM, n0 = nt * kBN;
+  grouped_tile(id / kPasses, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
+  const int i0 = rt * kBM + 32 * pass, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   int dst[kMI];  // output rows of this lane's active rows, loaded ahead
   if (kLast) {
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) dst[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
+    for (int mi = 0; mi < kBlocks; ++mi) dst[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
   }
   Acc acc;
   acc_zero(acc);
@@ -746,7 +758,7 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
     // continue the chain from the previous groups (rows/columns outside
     // the problem read a clamped, valid address; they are never stored)
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
+    for (int mi = 0; mi < kBlocks; ++mi) {
       const float* src = a.ghacc + (size_t)min(i0 + acc_row(wm, mi, lane), n_act - 1) * a.H;
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
@@ -762,7 +774,8 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const RowsK A = rows_k(a.dZ + (size_t)i0 * a.bg.ldz, kBM - 1, a.bg.ldz);
+  // (a pass's tile runs past the row tile; rows past dZ's last repeat it)
+  const RowsK A = rows_k(a.dZ + (size_t)i0 * a.bg.ldz, min(kBM - 1, a.bg.T_pad - 1 - i0), a.bg.ldz);
   WRowsMN B;
   B.base = reinterpret_cast<const char*>(a.W + n0);
   B.H = a.H;
@@ -772,9 +785,17 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
   B.V = a.gm.V;
 #pragma unroll
   for (int i = 0; i < kDma; ++i) B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
-  gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
+  if constexpr (kPart) {
+    const int wl = __builtin_amdgcn_readfirstlane(w);
+    if ((8 * kDma * wl) % kWaveRows < 32)  // this wave's load rows hold computed rows
+      gemm256<false, true, 1, true>(A, B, a.bg.ldz / kBK, acc, lds);
+    else
+      gemm256<false, true, 1, false>(A, B, a.bg.ldz / kBK, acc, lds);
+  } else {
+    gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
+  }
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi) {
+  for (int mi = 0; mi < kBlocks; ++mi) {
     const int i = i0 + acc_row(wm, mi, lane);
     if (i >= n_act) continue;
 #pragma unroll
@@ -800,18 +821,19 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 // ones) follow and fill the compute units that the grad_h tiles leave free,
 // then all of them as the grad_h tiles finish.  Either part is skipped when
 // its output pointer is NULL.
-template <bool kFirst, bool kLast>
+// kPart: grad_h tiles in row passes (see gradh_tile).
+template <bool kFirst, bool kLast, bool kPart>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void grad_tiles(GradHArgs ha,
                                                                                                GradWArgs wa) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*ha.n_act);
   const int rtiles = (n_act + kBM - 1) / kBM;
-  const int nh = ha.grad_h ? rtiles * ha.n_tiles : 0;
+  const int nh = ha.grad_h ? rtiles * ha.n_tiles * (kPart ? kMI : 1) : 0;
   const int nh_blocks = 8 * ((nh + 7) >> 3);
   const int bid = blockIdx.x;
   if (bid < nh_blocks) {
     const int id = xcd_tile(nh, bid);
-    if (id >= 0) gradh_tile<kFirst, kLast>(ha, id, rtiles, n_act, lds);
+    if (id >= 0) gradh_tile<kFirst, kLast, kPart>(ha, id, rtiles, n_act, lds);
     return;
   }
   // nh_blocks is a multiple of 8: block bid - nh_blocks runs on the same XCD

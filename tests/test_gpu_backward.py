@@ -155,6 +155,30 @@ def test_split_grouping_changes_no_bit(monkeypatch):
         assert torch.equal(gh, gh2) and torch.equal(gW, gW2), mb
 
 
+@pytest.mark.parametrize("T,H,V,budget_mb", [
+    (700, 256, 30000, None),    # one group of splits
+    (700, 256, 30000, "4"),     # several groups: the chain continues through the fp32 accumulator
+    (300, 512, 20000, None),    # ragged rows and a ragged last column tile of H
+])
+def test_grad_h_row_passes_change_no_bit(monkeypatch, T, H, V, budget_mb):
+    # grad_h tiles computed whole or in 32-row passes: the same MFMA chain
+    # per element, so the same bits
+    if budget_mb:
+        monkeypatch.setenv("RLK_DZ_BUDGET_MB", budget_mb)
+    inp = synth.make_inputs(T, H, V, 0.15)
+    h, W, y, g = dev_inputs(inp)
+    logp, lse = rlk.linear_logp_fwd(h, W, y)
+    out = {}
+    for passes in ("0", "1"):
+        monkeypatch.setenv("RLK_GRAD_H_PASSES", passes)
+        out[passes] = rlk.linear_logp_bwd(h, W, y, lse, g)
+        torch.cuda.synchronize()
+    say(f"  row passes T={T} H={H} V={V} budget={budget_mb}")
+    assert torch.equal(out["0"][0], out["1"][0]) and torch.equal(out["0"][1], out["1"][1])
+    ref_gh, _ = oracle.backward(inp.h, inp.W, inp.y, inp.g)
+    assert rel_l2(to64(out["1"][0]), ref_gh) <= GRAD_RTOL
+
+
 @pytest.mark.parametrize("T,H,V", [(3, 65536, 600), (5, 64, 8_000_000)])
 def test_maximum_hidden_and_vocabulary(T, H, V):
     say(f"bwd max sizes T={T} H={H} V={V}")
