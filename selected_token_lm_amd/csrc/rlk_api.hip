@@ -165,15 +165,17 @@ int device_cus() {
   return g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
 }
 
-// grad_h in row passes (gradh_tile's kPart) when its full tiles fit on the
-// compute units kMI times over, i.e. when each would otherwise run the
-// vocabulary-long chain alone while most units idle.  The environment
-// variable RLK_GRAD_H_PASSES = 0 / 1 forces either form (results are the
-// same bits; tests use it).
+// grad_h in two row passes (gradh_tile's kPart) when its whole tiles would
+// leave most compute units idle while each runs the vocabulary-long chain:
+// a pass's chain takes ~70 % of a tile's and the passes add ~40 % to
+// grad_h's work, which pays while three times the tile count fits on the
+// units (the grad_W tiles fill the rest).  The environment variable
+// RLK_GRAD_H_PASSES = 0 / 1 forces either form (results are the same bits;
+// tests use it).
 bool grad_h_passes(int64_t row_tiles, int64_t n_tiles) {
   const char* e = std::getenv("RLK_GRAD_H_PASSES");
   if (e && *e) return std::atoi(e) != 0;
-  return (int64_t)rlk::kMI * row_tiles * n_tiles <= device_cus();
+  return 3 * row_tiles * n_tiles <= device_cus();
 }
 
 // Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension.
@@ -490,7 +492,7 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
   // grids: every row tile of T (the kernels keep those of active rows)
   const int64_t dz_blocks = 8 * ceil_div(row_tiles * G * tps, 8);
   const bool passes = grad_h && grad_h_passes(row_tiles, n_tiles);
-  const int64_t gh_blocks = grad_h ? 8 * ceil_div(row_tiles * n_tiles * (passes ? rlk::kMI : 1), 8) : 0;
+  const int64_t gh_blocks = grad_h ? 8 * ceil_div(row_tiles * n_tiles * (passes ? 2 : 1), 8) : 0;
   const int64_t gw_blocks = grad_W ? 8 * ceil_div((int64_t)n_tiles * G * tps, 8) : 0;
   RLK_TRY(check_grid(dz_blocks));
   RLK_TRY(check_grid(gh_blocks + gw_blocks));

@@ -730,22 +730,24 @@ struct GradHArgs {
 // kFirst / kLast: the group is the first / last one (compile-time, so that
 // the accumulators never merge across a branch).  Tile id: (row tile, H tile).
 //
-// kPart: the tile's rows in kMI passes, id = kMI * tile + p.  Pass p reads
-// the dz tile from 32 p rows further down and every wave computes only its
-// first 32-row block, i.e. tile rows 32 p + kWaveRows wm + 0..31 (the
-// passes cover all of them); only the waves whose load rows meet those
-// rows load the dz tile.  kMI times the workgroups, each with 1 / kMI of
-// the MFMAs per k-block: for batches whose few grad_h tiles would each run
-// the vocabulary-long chain on a compute unit of their own while the
-// others idle.  Every element is the same MFMA chain as in a full tile.
+// kPart: the tile's rows in two passes, id = 2 tile + p.  Pass p reads the
+// dz tile from 16 kMI p rows further down and every wave computes only its
+// first kMI / 2 row blocks, i.e. tile rows 16 kMI p + kWaveRows wm + 0 ..
+// 16 kMI - 1 (the two passes cover all of them); only the waves whose load
+// rows meet those rows load the dz tile.  Twice the workgroups, each with
+// half the MFMAs per k-block and three quarters of the loads: the k-block
+// is then bound by its loads at ~70 % of a whole tile's time.  For
+// batches whose few grad_h tiles would each run the vocabulary-long chain
+// on a compute unit of their own while most units idle.  Every element is
+// the same MFMA chain as in a whole tile.
 template <bool kFirst, bool kLast, bool kPart>
 __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int n_act, u32x4* lds) {
-  constexpr int kPasses = kPart ? kMI : 1;
-  constexpr int kBlocks = kPart ? 1 : kMI;  // row blocks per wave
+  constexpr int kPasses = kPart ? 2 : 1;
+  constexpr int kBlocks = kMI / kPasses;  // row blocks per wave
   const int pass = id % kPasses;
   int rt, nt;
   grouped_tile(id / kPasses, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
-  const int i0 = rt * kBM + 32 * pass, n0 = nt * kBN;
+  const int i0 = rt * kBM + 32 * kBlocks * pass, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   int dst[kMI];  // output rows of this lane's active rows, loaded ahead
   if (kLast) {
@@ -786,11 +788,12 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 #pragma unroll
   for (int i = 0; i < kDma; ++i) B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
   if constexpr (kPart) {
+    static_assert(8 * kDma <= 32 * kBlocks && kWaveRows % (8 * kDma) == 0, "a wave's load rows in one half of its wave row");
     const int wl = __builtin_amdgcn_readfirstlane(w);
-    if ((8 * kDma * wl) % kWaveRows < 32)  // this wave's load rows hold computed rows
-      gemm256<false, true, 1, true>(A, B, a.bg.ldz / kBK, acc, lds);
+    if ((8 * kDma * wl) % kWaveRows < 32 * kBlocks)  // this wave's load rows hold computed rows
+      gemm256<false, true, kBlocks, true>(A, B, a.bg.ldz / kBK, acc, lds);
     else
-      gemm256<false, true, 1, false>(A, B, a.bg.ldz / kBK, acc, lds);
+      gemm256<false, true, kBlocks, false>(A, B, a.bg.ldz / kBK, acc, lds);
   } else {
     gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
   }
@@ -821,14 +824,14 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 // ones) follow and fill the compute units that the grad_h tiles leave free,
 // then all of them as the grad_h tiles finish.  Either part is skipped when
 // its output pointer is NULL.
-// kPart: grad_h tiles in row passes (see gradh_tile).
+// kPart: grad_h tiles in two row passes (see gradh_tile).
 template <bool kFirst, bool kLast, bool kPart>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void grad_tiles(GradHArgs ha,
                                                                                                GradWArgs wa) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*ha.n_act);
   const int rtiles = (n_act + kBM - 1) / kBM;
-  const int nh = ha.grad_h ? rtiles * ha.n_tiles * (kPart ? kMI : 1) : 0;
+  const int nh = ha.grad_h ? rtiles * ha.n_tiles * (kPart ? 2 : 1) : 0;
   const int nh_blocks = 8 * ((nh + 7) >> 3);
   const int bid = blockIdx.x;
   if (bid < nh_blocks) {
