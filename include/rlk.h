@@ -174,8 +174,8 @@ rlk_status rlk_linear_logp_bwd_saved(const void* h, const void* W, const int32_t
 /* Statistics of one vocabulary range [vocab_start, vocab_start + vocab_len)
  * of a vocabulary of V_global rows, as one tensor-parallel rank would hold it
  * ("Why the Fused Path Wins", third reason; "vLLM RL-Kernel v0.1.0 ...",
- * "Boundary Fixes in the RL-Kernel Strict Path": true vocabulary range,
- * target ownership, local reduction).
+ * "Boundary Fixes in the RL-Kernel Strict Path": the rank's real vocabulary
+ * rows, which rank owns a target, the reduction inside the rank).
  *   W_shard  bf16 [vocab_len, H]  rows vocab_start .. vocab_start+vocab_len-1
  *   y        int32 [T]            GLOBAL target ids
  *   out      [T]                  per-row statistics (rlk_lse_partial_t)
