@@ -61,12 +61,14 @@ def target_sweep():
     """Targets at every lane / element position of a 256-column tile and at
     the edges: H=128, V=20000, so a split is 625 columns = four full chunks
     and a 113-column chunk, and its third tile holds 113 columns (the second
-    128-column wave of that tile has none)."""
+    128-column wave of that tile has none); both sides of every split edge
+    (and so of every aligned block of splits a vocabulary shard can be)."""
     H, V = 128, 20000
     S = -(-V // 32)
     cols = list(range(256))                          # split 0, tile 0: every position
     cols += [256, 383, 384, 511, 512, 600, S - 1]    # tile 1, the short chunk, the split's end
-    cols += [S, 2 * S - 1, 16 * S, 31 * S + 511, 31 * S + 512, V - 2, V - 1]
+    cols += [31 * S + 511, 31 * S + 512, V - 2, V - 1]
+    cols += [c for b in range(1, 32) for c in (b * S - 1, b * S)]  # both sides of every split edge
     y = np.array(cols + [-100, -100], dtype=np.int32)
     inp = synth.make_inputs(len(y), H, V, 0.0, name="target_sweep")
     inp.y = y

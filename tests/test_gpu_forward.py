@@ -160,8 +160,11 @@ def test_bitwise_repeat():
         assert torch.equal(a, b) and torch.equal(la, lb)
 
 
-def test_partial_and_merge_match_forward_bitwise():
-    inp = synth.make_inputs(300, 128, 20000, 0.15)  # S = 625
+@pytest.mark.parametrize("sweep", [False, True])
+def test_partial_and_merge_match_forward_bitwise(sweep):
+    # V = 20000, S = 625; the sweep puts targets at every tile position and on
+    # the edges of splits and of the shards (the first and last row of each)
+    inp = target_sweep() if sweep else synth.make_inputs(300, 128, 20000, 0.15)
     h, W, y, _ = dev_inputs(inp)
     ref, ref_lse = rlk.linear_logp_fwd(h, W, y)
     V, S = inp.V, 625
