@@ -61,3 +61,18 @@ def test_random_shape_matches_oracle(monkeypatch, T, H, V, mask):
     assert err <= LOGP_TOL and err_lse <= LOGP_TOL
     assert e_h <= GRAD_RTOL and e_W <= GRAD_RTOL
     assert np.all(to64(logp)[~act] == 0.0)
+
+
+@pytest.mark.parametrize("T,H,V,mask", _shapes()[::3])
+def test_random_shape_save_logits_bitwise_equal_to_recompute(T, H, V, mask):
+    say(f"random shape, save-logits variant T={T} H={H} V={V} mask={mask}")
+    inp = synth.make_inputs(T, H, V, mask)
+    h, W, y, g = dev_inputs(inp)
+    logp0, lse0 = rlk.linear_logp_fwd(h, W, y)
+    gh0, gW0 = rlk.linear_logp_bwd(h, W, y, lse0, g)
+    logp1, lse1, z = rlk.linear_logp_fwd_save(h, W, y)
+    gh1, gW1 = rlk.linear_logp_bwd_saved(h, W, y, lse1, g, z)
+    torch.cuda.synchronize()
+    for a, b in ((logp0, logp1), (lse0, lse1), (gW0, gW1)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(gh0.view(torch.int16), gh1.view(torch.int16))
