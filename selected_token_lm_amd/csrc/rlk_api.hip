@@ -88,19 +88,20 @@ FwdWs fwd_layout(int64_t T, int64_t H, int64_t V) {
 }
 
 // Splits per backward group: the largest power of two G <= 32 whose dz
-// block (T_pad x G x S_pad bf16) fits the budget (default 1.25 GiB, env
-// RLK_DZ_BUDGET_MB overrides it, at most 2 GiB).  G changes no result bit,
-// only the workspace size and the number of launches.  The cap keeps the
-// per-lane byte offsets of a 256-row dz tile (255 rows x G x S_pad x 2 B,
-// below the budget) inside the 32 bits the tile loaders use.
+// block (T_pad x G x S_pad bf16) fits the budget (default 2.5 GiB, env
+// RLK_DZ_BUDGET_MB overrides it, at most 3.5 GiB).  G changes no result
+// bit, only the workspace size and the number of launches.  The cap keeps
+// the per-lane byte offsets of a 256-row dz tile (255 rows x G x S_pad x
+// 2 B, less than the block since T_pad >= 256) inside the 32 unsigned bits
+// the tile loaders use.
 int64_t dz_budget_bytes() {
-  constexpr int64_t kMaxBudget = int64_t(2048) << 20;
+  constexpr int64_t kMaxBudget = int64_t(3584) << 20;
   const char* e = std::getenv("RLK_DZ_BUDGET_MB");
   if (e && *e) {
     const long long mb = std::atoll(e);
     if (mb > 0) return std::min<int64_t>((int64_t)mb << 20, kMaxBudget);
   }
-  return (int64_t)1280 << 20;
+  return (int64_t)2560 << 20;
 }
 
 struct BwdWs {

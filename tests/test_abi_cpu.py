@@ -64,19 +64,21 @@ def test_workspace_bytes():
 
 
 def test_dz_budget_override_is_capped(monkeypatch):
-    # RLK_DZ_BUDGET_MB sets the backward's dz block budget up to 2 GiB; a
-    # larger value acts as 2 GiB (tile offsets stay 32-bit)
+    # RLK_DZ_BUDGET_MB sets the backward's dz block budget up to 3.5 GiB; a
+    # larger value acts as 3.5 GiB (tile offsets stay 32-bit)
     W = rlk.workspace_bytes
     shape = (1, 65536, 4096, 151936)  # one split's dz block: 2 * 65536 * 4800 B = 600 MiB
     monkeypatch.setenv("RLK_DZ_BUDGET_MB", "1024")
     one = W(*shape)
     monkeypatch.setenv("RLK_DZ_BUDGET_MB", "2048")
     two = W(*shape)
+    monkeypatch.setenv("RLK_DZ_BUDGET_MB", "3584")
+    four = W(*shape)
     monkeypatch.setenv("RLK_DZ_BUDGET_MB", "100000")
     big = W(*shape)
-    assert one < two == big
+    assert one < two < four == big
     per_split = 2 * 65536 * 4800
-    assert two - one == per_split  # G = 1 -> G = 2
+    assert two - one == per_split and four - two == 2 * per_split  # G = 1 -> 2 -> 4
 
 
 def fwd(h=FAKE, W=FAKE, y=FAKE, T=64, H=256, V=4096, logp=FAKE, lse=FAKE, ws=FAKE, nbytes=1 << 40):
