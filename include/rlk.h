@@ -104,7 +104,16 @@ const char* rlk_last_error_message(void);
 
 /* Workspace bytes needed by `op` (RLK_OP_*) for T rows, hidden size H and a
  * vocabulary of V rows (for RLK_OP_PARTIAL: V = V_global, the size of the
- * whole vocabulary).  Returns 0 for invalid arguments. */
+ * whole vocabulary).  Returns 0 for invalid arguments.
+ *
+ * The backward processes the vocabulary in groups of splits whose bf16 dz
+ * block (T rounded up to 256, times the group's padded columns) fits a
+ * budget of 2.5 GiB; the environment variable RLK_DZ_BUDGET_MB (read at
+ * every call, capped at 3584) sets another.  RLK_GRAD_H_PASSES = 0 / 1
+ * forces grad_h's whole-tile or row-pass form (chosen by batch size
+ * otherwise).  Neither changes a result bit; the budget changes the
+ * workspace size, so a caller that sets it must size the workspace under
+ * the same setting. */
 size_t rlk_workspace_bytes(int32_t op, int64_t T, int64_t H, int64_t V);
 
 /* Forward ("Announcing RL-Kernel for vime", "Key Capabilities": the
