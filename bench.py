@@ -330,10 +330,64 @@ def clock_power_window(torch, step, seconds=2.5, settle=0.75):
     return res
 
 
+def rocminfo_name(arch="gfx950"):
+    """Marketing name of the first `arch` agent that rocminfo lists, or None."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:  # no rocminfo on PATH, or it failed: report nothing
+        return None
+    for agent in txt.split("Agent ")[1:]:
+        fields = {}
+        for line in agent.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
+        if fields.get("Name", "").startswith(arch):
+            return fields.get("Marketing Name")
+    return None
+
+
+def amdsmi_names(torch):
+    """(market name, product name) of the benchmarked GPU from amdsmi, or Nones."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                    asic = amdsmi.amdsmi_get_gpu_asic_info(h)
+                    board = amdsmi.amdsmi_get_gpu_board_info(h)
+                    return asic.get("market_name"), board.get("product_name")
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:  # no amdsmi, no permission: report nothing
+        pass
+    return None, None
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
+    market, product = amdsmi_names(torch)
     # the clock and power under load come from ClockPowerSampler
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count}
+    return {"name": p.name, "rocminfo_marketing_name": rocminfo_name(), "amdsmi_market_name": market,
+            "amdsmi_product_name": product, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count}
+
+
+def host_cpu():
+    """(CPU model, the cores this process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
 
 
 def gemm_bench(args):
@@ -494,31 +548,76 @@ def rebatch_bench(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(inp, rows, backward):
+def _oracle_sample(inp, rows, backward):
+    """Times the fp64 oracle on the first `rows` rows of a workload (same W);
+    returns (seconds, logp, grad_h) of the sample."""
     import numpy as np
     import oracle
 
-    T = inp.T
     sel = np.arange(rows)
     hs, ys, gs = inp.h[sel], inp.y[sel], inp.g[sel]
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    oracle.forward(hs, inp.W, ys)
-    if backward:
-        oracle.backward(hs, inp.W, ys, gs)
-    dt = time.perf_counter() - t0
-    return {
-        "value": rows / dt,
-        "unit": "tokens/s",
-        "cores": int(cores),
-        "kind": "oracle",
-        "sample": f"first {rows} of the {T} rows ({int((ys != -100).sum())} active) through the fp64 "
-                  f"oracle's forward{' and backward' if backward else ''}, same W; {dt:.1f} s",
-    }
+    logp, _ = oracle.forward(hs, inp.W, ys)
+    gh = oracle.backward(hs, inp.W, ys, gs, want_grad_W=True)[0] if backward else None
+    return time.perf_counter() - t0, logp, gh
+
+
+def cpu_baseline(inp, rows, backward, gpu_logp=None, gpu_grad_h=None, other_configs=True):
+    """The fp64 oracle as it stands, on the host cores (all of this process's
+    CPU affinity, BLAS threads set to that count), on bounded samples: the
+    first `rows` rows of the benchmarked workload, and when `other_configs`
+    the Qwen3-8B-shaped forward and the Qwen3-30B-A3B-shaped forward +
+    backward on their first `rows` rows.  A reported baseline, not a target.
+    Also compares the GPU's outputs on the sample rows with the oracle's."""
+    import contextlib
+
+    import numpy as np
+
+    import synth
+
+    model, cores = host_cpu()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        limiter = contextlib.nullcontext()
+    with limiter:
+        dt, logp, gh = _oracle_sample(inp, rows, backward)
+        act = int((inp.y[:rows] != -100).sum())
+        res = {
+            "value": rows / dt,
+            "unit": "tokens/s",
+            "cores": int(cores),
+            "cpu_model": model,
+            "kind": "oracle",
+            "sample": f"first {rows} of the {inp.T} rows ({act} active) through the fp64 oracle's "
+                      f"forward{' and backward (grad_h and the sample rows full grad_W)' if backward else ''}, "
+                      f"same W; {dt:.1f} s",
+            "seconds": dt,
+        }
+        if gpu_logp is not None:
+            res["parity_on_sample"] = {"max_abs_dlogp": float(np.max(np.abs(gpu_logp[:rows] - logp)))}
+            if gh is not None and gpu_grad_h is not None:
+                a = inp.y[:rows] != -100
+                d = gpu_grad_h[:rows][a] - gh[a]
+                res["parity_on_sample"]["grad_h_rel_l2"] = float(np.linalg.norm(d) / np.linalg.norm(gh[a]))
+        if other_configs:
+            others = {}
+            for name, bwd in (("qwen3_8b", False), ("qwen3_30b_a3b", True)):
+                T, H, V, mask = synth.CONFIGS[name]
+                if (T, H, V) == (inp.T, inp.H, inp.V) and bwd == backward:
+                    continue
+                sub = synth.Inputs(name, rows, H, V, synth.normal_bf16(synth.SEED_H, rows, H),
+                                   inp.W if (H, V) == (inp.H, inp.V) else
+                                   synth.normal_bf16(synth.SEED_W, V, H, float(np.float32(1.0 / np.sqrt(H)))),
+                                   synth.targets(T, V, mask)[:rows], synth.upstream_grad(T)[:rows], mask)
+                t, _, _ = _oracle_sample(sub, rows, bwd)
+                others[f"{name}_{'fwd_bwd' if bwd else 'fwd'}"] = {
+                    "value": rows / t, "unit": "tokens/s", "seconds": t,
+                    "sample": f"first {rows} of the {T} rows (T={T}, H={H}, V={V}, "
+                              f"{int((sub.y != -100).sum())} active), forward{' and backward' if bwd else ''}"}
+            res["other_configs"] = others
+    return res
 
 
 def main():
@@ -530,6 +629,8 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(GEMM_WORKLOADS) + [REBATCH_WORKLOAD])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-other-configs", action="store_true",
+                    help="time the oracle on the benchmarked workload's sample only")
     ap.add_argument("--no-clock-power", action="store_true",
                     help="skip the extra steps that sample the GFX clock and socket power (use under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -581,10 +682,14 @@ def main():
     y = torch.from_numpy(inp.y).to(dev)
     g = torch.from_numpy(inp.g).to(dev)
     T_act = inp.n_active
+    # memory around the operator: everything it needs beyond its resident
+    # inputs (workspaces, outputs, the saved logits of the save-logits
+    # variant) counts, as in the pages' "peak reserved delta" of a call
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    reserved0 = torch.cuda.memory_reserved()
     ws_f = torch.empty(rlk.workspace_bytes(rlk.OP_FWD, T, H, V), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(rlk.workspace_bytes(rlk.OP_BWD, T, H, V), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    reserved0 = torch.cuda.memory_reserved()
 
     saved = args.workload.endswith("_saved")
     zsave = torch.empty((T, rlk.saved_logits_ld(V)), dtype=torch.float32, device=dev) if saved else None
@@ -594,45 +699,59 @@ def main():
         W_sh = [W[:half].contiguous(), W[half:].contiguous()]
         parts = torch.empty((2, T, 4), dtype=torch.float32, device=dev)
 
-    def step():
+    def step(keep=None):
+        """One step; `keep` (a dict) receives its logp and grad_h."""
+        gh = None
         if sharded:
             for r in range(2):
                 rlk.lse_partial(h, W_sh[r], y, r * half, V, ws=ws_f, out=parts[r])
-            rlk.lse_merge(parts, y)
-            return
-        if saved:
+            logp, _ = rlk.lse_merge(parts, y)
+        elif saved:
             logp, lse, _ = rlk.linear_logp_fwd_save(h, W, y, ws=ws_f, zsave=zsave)
-            rlk.linear_logp_bwd_saved(h, W, y, lse, g, zsave, ws=ws_b)
-            return
-        logp, lse = rlk.linear_logp_fwd(h, W, y, ws=ws_f)
-        if do_bwd:
-            rlk.linear_logp_bwd(h, W, y, lse, g, ws=ws_b)
+            gh, _ = rlk.linear_logp_bwd_saved(h, W, y, lse, g, zsave, ws=ws_b)
+        else:
+            logp, lse = rlk.linear_logp_fwd(h, W, y, ws=ws_f)
+            if do_bwd:
+                gh, _ = rlk.linear_logp_bwd(h, W, y, lse, g, ws=ws_b)
+        if keep is not None:
+            keep["logp"], keep["grad_h"] = logp, gh
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats()
-
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    rlk.profile_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for k in range(args.steps):
-        step_ev[k].record(stream)
-        step()
-    step_ev[args.steps].record(stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per_step = sorted(step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps))
-    kern = rlk.profile_end()
     peak_reserved = torch.cuda.max_memory_reserved()
+
+    stream = torch.cuda.current_stream()
+
+    def timed_pass(profile):
+        """K steps between synchronisations; per-step HIP events on the stream;
+        with `profile` every library launch is also bracketed by HIP events."""
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        if profile:
+            rlk.profile_begin()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for k in range(args.steps):
+            step_ev[k].record(stream)
+            step()
+        step_ev[args.steps].record(stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kern = rlk.profile_end() if profile else None
+        per = sorted(step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps))
+        return max((t1 - t0) * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps), per, kern
+
+    # headline: library timing off; then the same K steps with every launch
+    # timed by HIP events on its stream, for the per-kernel figures
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms, per_step, _ = timed_pass(False)
+    print(f"[bench] timing {args.steps} steps with per-kernel events", file=sys.stderr, flush=True)
+    ms_prof, _, kern = timed_pass(True)
     clock_power = None if args.no_clock_power or args.copy_calibration else clock_power_window(torch, step)
     if args.copy_calibration:
         copy_calibration(dev)
@@ -640,9 +759,6 @@ def main():
     # operands, no memory traffic): context for the roofline fraction
     ceiling = rlk.bench_mfma_ceiling()
 
-    ms_wall = (t1 - t0) * 1e3 / args.steps
-    ms_ev = ev0.elapsed_time(ev1) / args.steps
-    ms = max(ms_wall, ms_ev)
     # algorithmic contractions per step: forward, recompute (not in the
     # save-logits variant), grad_W, grad_h
     flops_step = 2.0 * T_act * H * V * ((3 if saved else 4) if do_bwd else 1)
@@ -692,6 +808,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "H": H, "V": V, "active_rows": T_act,
                    "ignore_index": -100, "parallelism": "single GPU"},
+        "active_tokens_per_s": T_act / (ms * 1e-3),
+        "ms_per_step_kernel_timing_pass": ms_prof,
         "step_ms_median_p10_p90": [per_step[len(per_step) // 2], per_step[len(per_step) // 10],
                                    per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)]],
         "device": device_info(torch),
@@ -711,14 +829,24 @@ def main():
                          "dominant_kernel_frac_of_ceiling": achieved / 1e12 / ceiling["median_tflops"]},
         "workspace_bytes": int(ws_f.numel() + (ws_b.numel() if do_bwd else 0)
                                + (zsave.numel() * 4 if saved else 0)),
+        "workspace_bytes_fwd_bwd": [int(ws_f.numel()), int(ws_b.numel()) if do_bwd else 0],
+        "dz_budget_mb_env": os.environ.get("RLK_DZ_BUDGET_MB"),
         "peak_reserved_delta_mb": (peak_reserved - reserved0) / 2**20,
+        "peak_reserved_delta_what": "torch max_memory_reserved after the warmup steps minus memory_reserved "
+                                    "before the workspaces were allocated: workspaces, outputs (logp, lse, "
+                                    "grad_h, grad_W) and saved logits, the inputs being resident before",
         "kernel_digest": kernel_digest(dom),
         "kernel_digests": {k: kernel_digest(k) for k in GEMM_KERNELS if k in kernels},
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_rows} rows)", file=sys.stderr, flush=True)
-        del h, W, y, g, ws_f, ws_b
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, do_bwd)
+        last = {}
+        step(last)
+        gpu_logp = last["logp"].cpu().numpy().astype(np.float64)
+        gpu_gh = last["grad_h"].float().cpu().numpy() if last["grad_h"] is not None else None
+        del h, W, y, g, ws_f, ws_b, last
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, do_bwd, gpu_logp, gpu_gh,
+                                           other_configs=not args.no_cpu_other_configs)
     print(json.dumps(out), flush=True)
 
 

@@ -45,7 +45,11 @@
  *   - outputs are overwritten, never accumulated;
  *   - host-detectable errors return a status and enqueue nothing; data errors
  *     the host cannot see (a target outside [0,V) that is not ignore_index,
- *     or no part owning an active target) give NaN in that row's logp;
+ *     or no part owning an active target) give NaN in that row's logp, and
+ *     in the backward NaN in that row's grad_h and in grad_W (the row's
+ *     loss is undefined, so is every gradient it reaches);
+ *   - H must be a multiple of 64 (the MFMA tile engine's k-block); the
+ *     Qwen3 LM-head shapes (H = 2048, 4096) are;
  *   - T == 0 returns RLK_OK without launching anything (after the shape
  *     checks); row-indexed pointers may then be NULL.
  */
@@ -140,7 +144,9 @@ rlk_status rlk_linear_logp_fwd(const void* h, const void* W, const int32_t* y,
  *                          rounded to bf16 once; zero rows for inactive rows;
  *                          may be NULL (not computed)
  *   grad_W  fp32 [V,H] out written once per element; may be NULL
- * Row ordering: grad_W sums rows in ascending row order. */
+ * Row ordering: grad_W sums rows in ascending row order.
+ * An active row whose target lies outside [0, V) makes its grad_h row NaN
+ * and, since every grad_W element sums over all active rows, grad_W NaN. */
 rlk_status rlk_linear_logp_bwd(const void* h, const void* W, const int32_t* y,
                                const float* lse, const float* g,
                                int64_t T, int64_t H, int64_t V, int32_t ignore_index,
@@ -254,34 +260,6 @@ enum { RLK_DT_F32 = 0, RLK_DT_BF16 = 1 };
  * ldc % 4 == 0; M == 0 or N == 0 returns RLK_OK without launching. */
 rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                             void* C, int64_t ldc, int32_t c_dtype, void* stream);
-
-/* Benchmark only (computes nothing of the operator): runs `blocks`
- * workgroups of 4 waves, each wave issuing iters * 64
- * v_mfma_f32_32x32x16_bf16 on a 128 x 128 accumulator tile with operands
- * cycled through 4 register sets of random bf16 data, and no memory traffic
- * in the loop: the MFMA throughput the part sustains under its power limit
- * with realistic operand toggling (2 * 32 * 32 * 16 FLOP per instruction).
- *   src  bf16 device buffer of 32 * 256 * 8 values (random; 16-byte aligned)
- *   out  fp32 [blocks * 256] out (sums of the accumulators, so nothing is
- *        optimised away) */
-rlk_status rlk_bench_mfma_ceiling(const void* src, float* out, int32_t blocks, int32_t iters,
-                                  void* stream);
-
-/* Per-kernel timing for benchmarks; computes nothing.  After
- * rlk_profile_begin(), every kernel the library launches (on any stream) is
- * bracketed by two HIP events recorded on that stream.  rlk_profile_end()
- * waits for those events, turns timing off and writes up to max_entries
- * per-kernel totals to `out` (launch count and summed event time in ms);
- * *n_entries receives the number of distinct kernels seen.  Not meant to be
- * used from several threads at once. */
-typedef struct {
-  char name[40];
-  int64_t launches;
-  double total_ms;
-} rlk_kernel_time_t;
-
-rlk_status rlk_profile_begin(void);
-rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t* n_entries);
 
 #ifdef __cplusplus
 }

@@ -124,16 +124,39 @@ def _stream():
 
 
 def _prep(h, W, y):
-    if not (h.is_cuda and W.is_cuda and y.is_cuda):
-        raise ValueError("h, W and y must be device tensors")
+    """Shapes and dtypes first, then the device, so that a malformed call
+    fails in Python before any kernel can read past a short tensor."""
     if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("h and W must be bfloat16")
     if h.dim() != 2 or W.dim() != 2 or h.shape[1] != W.shape[1]:
         raise ValueError("h must be [T, H] and W [V, H]")
-    y = y.to(torch.int32) if y.dtype != torch.int32 else y
     if y.dim() != 1 or y.shape[0] != h.shape[0]:
-        raise ValueError("y must be [T]")
+        raise ValueError(f"y must be [T] = [{h.shape[0]}], got {list(y.shape)}")
+    if y.dtype not in (torch.int32, torch.int64):
+        raise TypeError("y must hold int32 or int64 target ids")
+    if not (h.is_cuda and W.is_cuda and y.is_cuda):
+        raise ValueError("h, W and y must be device tensors")
+    if W.device != h.device or y.device != h.device:
+        raise ValueError("h, W and y must be on one device")
+    y = y.to(torch.int32) if y.dtype != torch.int32 else y
     return h.contiguous(), W.contiguous(), y.contiguous()
+
+
+def _rows(T, device, **named):
+    """Per-row tensors: each 1-D of length T (checked for all of them first),
+    then each on `device`; returned contiguous, int32 for `y`, else float32.
+    The kernels read element t for every row t < T, so a shorter tensor would
+    be read out of bounds on the device."""
+    for name, t in named.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.dim() != 1 or t.shape[0] != T:
+            raise ValueError(f"{name} must be 1-D of length T = {T}, got shape {list(t.shape)}")
+    for name, t in named.items():
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be on {device}")
+    out = [t.to(torch.int32 if name == "y" else torch.float32).contiguous() for name, t in named.items()]
+    return out if len(out) > 1 else out[0]
 
 
 def _workspace(op, T, H, V, device):
@@ -141,6 +164,14 @@ def _workspace(op, T, H, V, device):
     if n == 0:
         raise ValueError(f"invalid shape T={T} H={H} V={V}")
     return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def _given_workspace(ws, device):
+    """A caller's workspace: a contiguous byte tensor on `device` (the
+    library checks its size against rlk_workspace_bytes)."""
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"ws must be a contiguous uint8 tensor on {device}")
+    return ws, ws.numel()
 
 
 def linear_logp_fwd(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None):
@@ -153,7 +184,7 @@ def linear_logp_fwd(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None):
     if ws is None:
         ws, n = _workspace(OP_FWD, T, H, V, h.device)
     else:
-        n = ws.numel()
+        ws, n = _given_workspace(ws, h.device)
     _check(lib().rlk_linear_logp_fwd(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
                                      _ptr(logp), _ptr(lse), _ptr(ws), n, _stream()),
            "rlk_linear_logp_fwd")
@@ -166,14 +197,13 @@ def linear_logp_bwd(h, W, y, lse, g, ignore_index: int = IGNORE_INDEX,
     h, W, y = _prep(h, W, y)
     T, H = h.shape
     V = W.shape[0]
-    lse = lse.to(torch.float32).contiguous()
-    g = g.to(torch.float32).contiguous()
+    lse, g = _rows(T, h.device, lse=lse, g=g)
     grad_h = torch.empty((T, H), dtype=torch.bfloat16, device=h.device) if need_grad_h else None
     grad_W = torch.empty((V, H), dtype=torch.float32, device=h.device) if need_grad_W else None
     if ws is None:
         ws, n = _workspace(OP_BWD, T, H, V, h.device)
     else:
-        n = ws.numel()
+        ws, n = _given_workspace(ws, h.device)
     _check(lib().rlk_linear_logp_bwd(_ptr(h), _ptr(W), _ptr(y), _ptr(lse), _ptr(g), T, H, V,
                                      ignore_index, _ptr(grad_h), _ptr(grad_W), _ptr(ws), n,
                                      _stream()),
@@ -203,7 +233,7 @@ def linear_logp_fwd_save(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None, zsa
     if ws is None:
         ws, n = _workspace(OP_FWD, T, H, V, h.device)
     else:
-        n = ws.numel()
+        ws, n = _given_workspace(ws, h.device)
     _check(lib().rlk_linear_logp_fwd_save(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
                                           _ptr(logp), _ptr(lse), _ptr(zsave), zsave.stride(0),
                                           _ptr(ws), n, _stream()),
@@ -217,16 +247,16 @@ def linear_logp_bwd_saved(h, W, y, lse, g, zsave, ignore_index: int = IGNORE_IND
     h, W, y = _prep(h, W, y)
     T, H = h.shape
     V = W.shape[0]
-    lse = lse.to(torch.float32).contiguous()
-    g = g.to(torch.float32).contiguous()
-    if zsave.dtype != torch.float32 or zsave.dim() != 2 or zsave.stride(1) != 1:
+    lse, g = _rows(T, h.device, lse=lse, g=g)
+    if (zsave.dtype != torch.float32 or zsave.dim() != 2 or zsave.stride(1) != 1
+            or zsave.shape[0] != T or zsave.stride(0) < saved_logits_ld(V) or zsave.device != h.device):
         raise ValueError("zsave must be the float32 [T, ld] buffer of linear_logp_fwd_save")
     grad_h = torch.empty((T, H), dtype=torch.bfloat16, device=h.device) if need_grad_h else None
     grad_W = torch.empty((V, H), dtype=torch.float32, device=h.device) if need_grad_W else None
     if ws is None:
         ws, n = _workspace(OP_BWD, T, H, V, h.device)
     else:
-        n = ws.numel()
+        ws, n = _given_workspace(ws, h.device)
     _check(lib().rlk_linear_logp_bwd_saved(_ptr(h), _ptr(W), _ptr(y), _ptr(lse), _ptr(g), _ptr(zsave),
                                            zsave.stride(0), T, H, V, ignore_index, _ptr(grad_h),
                                            _ptr(grad_W), _ptr(ws), n, _stream()),
@@ -251,7 +281,7 @@ def lse_partial(h, W_shard, y, vocab_start: int, V_global: int,
     if ws is None:
         ws, n = _workspace(OP_PARTIAL, T, H, V_global, h.device)
     else:
-        n = ws.numel()
+        ws, n = _given_workspace(ws, h.device)
     _check(lib().rlk_lse_partial(_ptr(h), _ptr(W_shard), _ptr(y), T, H, vocab_start, n_rows,
                                  V_global, ignore_index, _ptr(out), _ptr(ws), n, _stream()),
            "rlk_lse_partial")
@@ -262,9 +292,11 @@ def lse_merge(parts, y, ignore_index: int = IGNORE_INDEX):
     """Merge [P, T, 4] range statistics (ascending vocabulary order) into (logp, lse)."""
     if parts.dim() != 3 or parts.shape[2] != 4 or parts.dtype != torch.float32:
         raise ValueError("parts must be float32 [P, T, 4]")
-    y = (y.to(torch.int32) if y.dtype != torch.int32 else y).contiguous()
+    if not parts.is_cuda:
+        raise ValueError("parts must be a device tensor")
     parts = parts.contiguous()
     P, T = parts.shape[0], parts.shape[1]
+    y = _rows(T, parts.device, y=y)
     logp = torch.empty(T, dtype=torch.float32, device=parts.device)
     lse = torch.empty(T, dtype=torch.float32, device=parts.device)
     _check(lib().rlk_lse_merge(_ptr(parts), P, _ptr(y), T, ignore_index, _ptr(logp), _ptr(lse),
@@ -301,14 +333,19 @@ def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float 
                   beta: float = 0.0, logp_ref=None, scale: float = 1.0,
                   ignore_index: int = IGNORE_INDEX):
     """Per-token clipped-surrogate + k3-KL loss and g = dloss/dlogp, fp32 [T] each."""
-    def f32(x):
-        if not x.is_cuda:
-            raise ValueError("inputs must be device tensors")
-        return x.to(torch.float32).contiguous()
-    logp, logp_old, adv = f32(logp), f32(logp_old), f32(adv)
-    ref = f32(logp_ref) if logp_ref is not None else None
-    y = (y.to(torch.int32) if y.dtype != torch.int32 else y).contiguous()
+    if logp.dim() != 1:
+        raise ValueError("logp must be 1-D")
+    if beta != 0.0 and logp_ref is None:
+        raise ValueError("logp_ref is required when beta != 0")
     T = logp.shape[0]
+    named = dict(logp=logp, logp_old=logp_old, adv=adv, y=y)
+    if logp_ref is not None:
+        named["logp_ref"] = logp_ref
+    checked = dict(zip(named, _rows(T, logp.device, **named)))
+    logp, logp_old, adv, y = checked["logp"], checked["logp_old"], checked["adv"], checked["y"]
+    ref = checked.get("logp_ref")
+    if not logp.is_cuda:
+        raise ValueError("inputs must be device tensors")
     loss = torch.empty(T, dtype=torch.float32, device=logp.device)
     g = torch.empty(T, dtype=torch.float32, device=logp.device)
     _check(lib().rlk_rl_token_loss(_ptr(logp), _ptr(logp_old), _ptr(adv), _ptr(ref), _ptr(y), T,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -13,6 +14,7 @@
 #include <vector>
 
 #include "rlk.h"
+#include "rlk_bench.h"
 #include "rlk_kernels.h"
 
 namespace {
@@ -198,7 +200,9 @@ struct ProfRec {
   hipEvent_t start, stop;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+// read without the lock on every launch: when timing is off (the normal
+// case) a launch takes no lock at all
+std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -219,8 +223,9 @@ struct ProfScope {
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(const char* n, hipStream_t s) : name(n), st(s) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
     a = prof_event();
     b = prof_event();
     if (a && b) {
@@ -315,7 +320,7 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, yA, n_act,
              mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
   RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, static_cast<const uint16_t*>(h), idx, n_act,
-             (int)H, y, nullptr, nullptr, hA, nullptr);
+             (int)H, (int)V_global, y, nullptr, nullptr, hA, nullptr);
 
   rlk::SplitGeom gm;
   gm.V = (int)g.V;
@@ -473,7 +478,8 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, nullptr, n_act, nullptr, nullptr,
              nullptr);
-  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, y, lse, g, hA, rowinfo);
+  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, (int)V, y, lse, g, hA,
+             rowinfo);
   if (grad_h) {
     RLK_LAUNCH(zero_rows, dim3((unsigned)T), dim3(256), st, y, ignore_index, (int)H, static_cast<uint16_t*>(grad_h));
   }
@@ -676,13 +682,13 @@ rlk_status rlk_profile_begin(void) {
     g_prof_pool.push_back(r.stop);
   }
   g_prof_recs.clear();
-  g_prof_on = true;
+  g_prof_on.store(true);
   return ok();
 }
 
 rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t* n_entries) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = false;
+  g_prof_on.store(false);
   std::vector<rlk_kernel_time_t> acc;
   rlk_status st = RLK_OK;
   for (auto& r : g_prof_recs) {
@@ -709,3 +715,4 @@ rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t*
 }
 
 }  // extern "C"
+

@@ -992,9 +992,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 
 // hA[i] = h[idx[i]] for active rows i < n_act, zero rows for n_act <= i <
 // rows; rowinfo (optional) [i] = {lse, g, target, 0} of the row ({0, 0, -1,
-// 0} past n_act).  grid rows, block 256; 16-byte pieces.
+// 0} past n_act).  An active row whose target lies outside [0, V) has no
+// defined log-probability (the forward wrote NaN for it): its g becomes NaN,
+// so that the backward's gradients show it (NaN in the row's grad_h and in
+// every grad_W element it reaches) instead of silently dropping the target
+// term.  grid rows, block 256; 16-byte pieces.
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
-                                                   const int32_t* __restrict__ n_act_p, int H,
+                                                   const int32_t* __restrict__ n_act_p, int H, int V,
                                                    const int32_t* __restrict__ y, const float* __restrict__ lse,
                                                    const float* __restrict__ g, uint16_t* __restrict__ hA,
                                                    float4* __restrict__ rowinfo) {
@@ -1005,7 +1009,11 @@ __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ 
     const int t = idx[i];
     const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)t * H);
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
-    if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(lse[t], g[t], __int_as_float(y[t]), 0.f);
+    if (rowinfo && threadIdx.x == 0) {
+      const int yt = y[t];
+      const float gt = (yt >= 0 && yt < V) ? g[t] : __builtin_nanf("");
+      rowinfo[i] = make_float4(lse[t], gt, __int_as_float(yt), 0.f);
+    }
   } else {
     for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
     if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
