@@ -237,6 +237,25 @@ rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const flo
                              int32_t ignore_index, float eps_low, float eps_high, float beta,
                              float scale, float* loss, float* g, void* stream);
 
+/* The forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results
+ * (bit for bit) as rlk_linear_logp_fwd, but the workspace is a fixed
+ * device array inside the library: RLK_NOALLOC_SCRATCH_BYTES per GPU,
+ * allocated when the library's code is loaded on that GPU and held until
+ * the process ends.  Calls whose workspace (rlk_workspace_bytes(RLK_OP_FWD,
+ * T, H, V)) exceeds it return RLK_ERR_WORKSPACE_TOO_SMALL and enqueue
+ * nothing -- e.g. up to about 3700 rows at H = 4096, V = 151936.  Every call
+ * on one GPU uses the same scratch: calls that may run at the same time on
+ * one GPU (different streams, different host threads) race and must be
+ * ordered by the caller.  The scratch keeps the last call's contents;
+ * nothing in it needs to start at zero.  Allocates nothing, on the host
+ * side either. */
+#define RLK_NOALLOC_SCRATCH_BYTES (64u << 20)
+rlk_status rlk_linear_logp_fwd_noalloc(const void* h, const void* W, const int32_t* y,
+                                       int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                                       float* logp, float* lse, void* stream);
+
 /* Output element types of rlk_gemm_bf16_nt. */
 enum { RLK_DT_F32 = 0, RLK_DT_BF16 = 1 };
 

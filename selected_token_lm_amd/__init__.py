@@ -27,6 +27,7 @@ __all__ = [
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
     "lse_merge", "linear_logp", "gemm_bf16_nt", "linear_logp_fwd_save", "linear_logp_bwd_saved",
     "saved_logits_ld", "rl_token_loss", "profile_begin", "profile_end",
+    "linear_logp_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 IGNORE_INDEX = -100
@@ -66,6 +67,9 @@ _SIGNATURES = {
     "rlk_rl_token_loss": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                  _c_void_p, _c_void_p, _c_void_p]),
+    "rlk_linear_logp_fwd_noalloc": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                                           _c_void_p, _c_void_p, _c_void_p]),
+    # benchmark helpers (include/rlk_bench.h)
     "rlk_bench_mfma_ceiling": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p]),
     "rlk_profile_begin": (_i32, []),
     "rlk_profile_end": (_i32, [_c_void_p, _i32, ctypes.POINTER(_i32)]),
@@ -188,6 +192,30 @@ def linear_logp_fwd(h, W, y, ignore_index: int = IGNORE_INDEX, ws=None):
     _check(lib().rlk_linear_logp_fwd(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
                                      _ptr(logp), _ptr(lse), _ptr(ws), n, _stream()),
            "rlk_linear_logp_fwd")
+    return logp, lse
+
+
+# Size of the library's fixed device scratch (RLK_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_logp_fwd_noalloc(h, W, y, ignore_index: int = IGNORE_INDEX, logp=None, lse=None):
+    """linear_logp_fwd without a workspace: the library's fixed device scratch
+    serves instead (nothing is allocated when logp and lse are given).  Calls
+    on one GPU share that scratch and must not overlap."""
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    if logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=h.device)
+    if lse is None:
+        lse = torch.empty(T, dtype=torch.float32, device=h.device)
+    for name, t in (("logp", logp), ("lse", lse)):
+        if t.dtype != torch.float32 or t.shape != (T,) or not t.is_contiguous() or t.device != h.device:
+            raise ValueError(f"{name} must be a contiguous float32 [T] tensor on {h.device}")
+    _check(lib().rlk_linear_logp_fwd_noalloc(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
+                                             _ptr(logp), _ptr(lse), _stream()),
+           "rlk_linear_logp_fwd_noalloc")
     return logp, lse
 
 

@@ -716,3 +716,62 @@ rlk_status rlk_profile_end(rlk_kernel_time_t* out, int32_t max_entries, int32_t*
 
 }  // extern "C"
 
+
+// --- forward with a fixed device scratch (rlk_linear_logp_fwd_noalloc) --------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): the forward's workspace lives in this
+// file-scope device array instead of a caller buffer.  Every GPU the library
+// runs on holds one copy of it until the process ends.  In host code the name
+// `scratch` is only a stand-in: its device address on the current GPU comes
+// from hipGetSymbolAddress, looked up once per device and kept below.
+__device__ __align__(256) unsigned char scratch[RLK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // device address of `scratch` per device; NULL until looked up
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current).
+rlk_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RLK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(RLK_ERR_UNSUPPORTED_DEVICE, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RLK_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return RLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_linear_logp_fwd_noalloc(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H,
+                                       int64_t V, int32_t ignore_index, float* logp, float* lse, void* stream) {
+  RLK_TRY(check_common(h, W, y, T, H, V));
+  if (T == 0) return ok();
+  if (!logp) return fail(RLK_ERR_NULL_ARG, "logp is required");
+  if (!aligned16(logp) || (lse && !aligned16(lse))) return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse must be 16-byte aligned");
+  const size_t need = fwd_layout(T, H, V).total;
+  if (need > (size_t)RLK_NOALLOC_SCRATCH_BYTES)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL,
+                "T=%lld H=%lld V=%lld needs %zu bytes of scratch; the fixed device scratch holds %zu "
+                "(use rlk_linear_logp_fwd with a workspace)",
+                (long long)T, (long long)H, (long long)V, need, (size_t)RLK_NOALLOC_SCRATCH_BYTES);
+  RLK_TRY(check_device());
+  void* ws = nullptr;
+  RLK_TRY(scratch_address(&ws));
+  RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
+                      static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     # the benchmark helpers live in their own header, apart from the operator's ABI
     bench = declared_functions([os.path.join(ROOT, "include", "rlk_bench.h")])
     assert bench == ["rlk_bench_mfma_ceiling", "rlk_profile_begin", "rlk_profile_end"], bench
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -227,3 +227,20 @@ def test_binding_refuses_host_tensors():
     h = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rlk.linear_logp_fwd(h, h, torch.zeros(4, dtype=torch.int32))
+
+
+def test_noalloc_validation():
+    L = rlk.lib()
+
+    def call(T=64, H=256, V=4096, h=FAKE, logp=FAKE, lse=FAKE):
+        return L.rlk_linear_logp_fwd_noalloc(h, FAKE, FAKE, T, H, V, -100, logp, lse, None)
+
+    assert rlk.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert call(logp=None) == NULL_ARG
+    assert call(H=96) == BAD_SHAPE
+    assert call(lse=MISALIGNED) == BAD_ALIGN
+    assert call(T=0, h=None, logp=None, lse=None) == OK
+    # more workspace than the fixed scratch holds: refused on the host
+    assert rlk.workspace_bytes(0, 4096, 4096, 151936) > rlk.NOALLOC_SCRATCH_BYTES
+    assert call(T=4096, H=4096, V=151936) == WS_SMALL
+    assert b"fixed device scratch" in L.rlk_last_error_message()
