@@ -412,13 +412,13 @@ struct NoTail {
   __device__ __forceinline__ void operator()() const {}
 };
 
+//
+// nk >= 1 (callers with a possibly empty K skip the call: an early return
+// here would join an all-zero accumulator path into the epilogue and make
+// the register allocator shuffle, and spill, the accumulators).
 template <bool A_MN, bool B_MN, int kRB = kMI, bool kLoadA = true, class LA, class LB, class Tail = NoTail>
 __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds,
                                         const Tail& tail = Tail{}) {
-  if (nk <= 0) {
-    tail();
-    return;
-  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = kWaveRows * wave_m(w), rb0 = 128 * wave_n(w);
   static_assert(kKK == 4 && kSlots == 5, "schedule written for four k steps and five tile slots");

@@ -93,6 +93,21 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
   c1 = min(c0 + kChunk, send);
 }
 
+// sum over k in [k0, k0 + N) of e(v[k] - m) as a balanced pairwise tree
+// (adjacent pairs, then pairs of pairs): the same additions as tree_sum64
+// on those values, evaluated subtree by subtree so that only one partial
+// sum per level is live.
+template <int N>
+__device__ __forceinline__ float exp_tree(const float (&v)[64], int k0, float m) {
+  if constexpr (N == 1) {
+    return rlk_exp(v[k0] - m);
+  } else {
+    const float l = exp_tree<N / 2>(v, k0, m);
+    const float r = exp_tree<N / 2>(v, k0 + N / 2, m);
+    return l + r;
+  }
+}
+
 // Balanced pairwise tree over e[0..63]: adjacent pairs, then pairs of pairs.
 // (Fixed-size levels: every index is a compile-time constant.)
 __device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
@@ -136,10 +151,7 @@ __device__ __forceinline__ float2 chunk_stats(const float (&v)[64]) {
   float lo, hi;
   lane_halves(mx, lo, hi);
   mx = fmaxf(lo, hi);
-  float e[64];
-#pragma unroll
-  for (int k = 0; k < 64; ++k) e[k] = rlk_exp(v[k] - mx);
-  lane_halves(tree_sum64(e), lo, hi);
+  lane_halves(exp_tree<64>(v, 0, mx), lo, hi);
   return make_float2(mx, lo + hi);
 }
 
@@ -257,20 +269,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
       // columns cc0 + 32 ni + 8 q + 4 hh + 0..3 (the chunk's first `width`);
       // cc0 - sbeg is a multiple of 128, so every float4 is 16-byte aligned
       float* zr = a.zsave + (size_t)trow[mi] * a.ldzs + (size_t)(a.gm.s0 + sl) * a.zs_spad + (cc0 - sbeg) + 4 * hh;
+      if (width == kChunk) {
+        // a whole chunk (wave-uniform): every float4 is inside it
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
+        for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = 32 * ni + 8 * q;  // column of element 0, relative to cc0 + 4 hh
-          const float* e = v + 16 * ni + 4 * q;
-          if (c + 4 <= lim) {
-            *reinterpret_cast<float4*>(zr + c) = make_float4(e[0], e[1], e[2], e[3]);
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (c + u < lim) zr[c + u] = e[u];
+          for (int q = 0; q < 4; ++q) {
+            const float* e = v + 16 * ni + 4 * q;
+            *reinterpret_cast<float4*>(zr + 32 * ni + 8 * q) = make_float4(e[0], e[1], e[2], e[3]);
           }
-        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 32 * ni + 8 * q;  // column of element 0, relative to cc0 + 4 hh
+            const float* e = v + 16 * ni + 4 * q;
+            if (c + 4 <= lim) {
+              *reinterpret_cast<float4*>(zr + c) = make_float4(e[0], e[1], e[2], e[3]);
+            } else {
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (c + u < lim) zr[c + u] = e[u];
+            }
+          }
+      }
     }
     // target logit: rare (a row's target lies in a given chunk about once in
     // a thousand).  When some lane of the wave needs one, the wave's values
@@ -289,19 +312,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
       }
     }
     // the short last chunk of a split (a wave-uniform branch): its missing
-    // columns as -inf, in a copy, so that only (m, s) leaves either branch
-    float2 st;
+    // columns become -inf in place (v is this row block's own copy and is
+    // not used after the statistics)
     if (width < kChunk) {
-      float u[64];
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          u[16 * ni + r] = 32 * ni + 8 * (r >> 2) + (r & 3) < lim ? v[16 * ni + r] : -INFINITY;
-      st = chunk_stats(u);
-    } else {
-      st = chunk_stats(v);
+          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) v[16 * ni + r] = -INFINITY;
     }
+    const float2 st = chunk_stats(v);
     if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = st;
   }
 }
@@ -379,10 +399,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
 
 // ---------------------------------------------------------------------------
 // rlk_lse_merge: per row, balanced tree over n_parts range statistics.
-// The tree: left subtree = the largest power of two below the count.  The
-// count is decomposed into power-of-two blocks from the front (its binary
-// digits, most significant first); each block is a pairwise tree and the
-// blocks are combined right to left: B1 (+) (B2 (+) (B3 ...)).
+// The tree: left subtree = the largest power of two below the count.  That
+// is the pairwise tree over 32 slots (adjacent pairs, then pairs of pairs)
+// with the slots past n_parts holding the empty statistics: combining with
+// the empty statistics returns the other operand bit for bit, so the padded
+// subtrees reduce to exactly the unpadded ones.  (Every index is a
+// compile-time constant, so the 32 records stay in registers.)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict__ parts, int n_parts, int T,
                                                    const int32_t* __restrict__ y, int ignore_index,
@@ -397,6 +419,7 @@ __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict_
   MS v[kNSplit];
   int owners = 0;
   float z = 0.f;
+#pragma unroll
   for (int p = 0; p < kNSplit; ++p) {
     if (p < n_parts) {
       const PartialRec r = parts[(size_t)p * T + t];
@@ -409,20 +432,11 @@ __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict_
       v[p] = ms_identity();
     }
   }
-  MS acc = ms_identity();
-  bool first = true;
-  int end = n_parts;
-  for (int bit = 0; bit < 6; ++bit) {
-    if (!((n_parts >> bit) & 1)) continue;
-    const int size = 1 << bit;
-    const int lo = end - size;
-    end = lo;
-    // pairwise tree over v[lo .. lo+size)
-    for (int w = 1; w < size; w <<= 1)
-      for (int s = lo; s + w < lo + size; s += 2 * w) v[s] = ms_combine(v[s], v[s + w]);
-    acc = first ? v[lo] : ms_combine(v[lo], acc);
-    first = false;
-  }
+#pragma unroll
+  for (int w = 1; w < kNSplit; w <<= 1)
+#pragma unroll
+    for (int s = 0; s + w < kNSplit; s += 2 * w) v[s] = ms_combine(v[s], v[s + w]);
+  const MS acc = v[0];
   const float L = rlk_log(acc.s);
   logp[t] = (owners == 1) ? (z - acc.m) - L : __builtin_nanf("");
   if (lse) lse[t] = acc.m + L;
@@ -483,9 +497,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   for (int mi = 0; mi < kMI; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, lane)];
   Acc acc;
   acc_zero(acc);
-  if (c0 < c1) {
+  {
+    // a tile past the vocabulary (tiny vocabularies only: c0 >= c1) still
+    // runs, on W's first row; its columns are all written as zeros below
     const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
-    const RowsK B = rows_k(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H);
+    const RowsK B = c0 < c1 ? rows_k(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H) : rows_k(a.W, 0, a.H);
     gemm256<false, false>(A, B, a.H / kBK, acc, lds);
   }
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
@@ -691,7 +707,8 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
   const ColsMN B = cols_mn(a.hA, n0, a.H, a.H);
   Acc acc;
   acc_zero(acc);
-  gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
+  // no active rows: grad_W is zero
+  if (n_act > 0) gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
   const int lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
   float* out = a.grad_W + (size_t)sbeg * a.H;
 #pragma unroll

@@ -47,6 +47,15 @@ def compute():
     S = -(-inp.V // 32)
     parts = [rlk.lse_partial(h, W[a:a + 16 * S], y, a, inp.V) for a in (0, 16 * S)]
     out["small_partials"] = {"shard0": digest(parts[0]), "shard1": digest(parts[1])}
+    # merges of counts that are not powers of two (aligned blocks of 16, 8, 8
+    # and of 8, 8, 8, 4, 4 splits)
+    for name, widths in (("merge3", (16, 8, 8)), ("merge5", (8, 8, 8, 4, 4))):
+        starts = np.cumsum((0,) + widths[:-1])
+        ps = [rlk.lse_partial(h, W[a * S:min((a + n) * S, inp.V)], y, int(a * S), inp.V)
+              for a, n in zip(starts, widths)]
+        lp, ls = rlk.lse_merge(torch.stack(ps), y)
+        out["small_partials"][name + "_logp"] = digest(lp)
+        out["small_partials"][name + "_lse"] = digest(ls)
     # the RL objective on those log-probabilities
     gen = np.random.Generator(np.random.PCG64(11))
     old = f32_dev(inp_logp_shift(gen, logp.cpu().numpy()))
