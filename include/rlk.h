@@ -226,7 +226,9 @@ rlk_status rlk_lse_merge(const rlk_lse_partial_t* parts, int32_t n_parts,
  *     loss = scale * ( -min(r*adv, c*adv) + beta * ((e(d) - d) - 1) ),  d = logp_ref - logp
  *     g    = scale * ( (r*adv <= c*adv ? -r*adv : 0) + beta * (1 - e(d)) )
  * fp32, each operation rounded once in the order written, e() the
- * library's exp.  Rows with y == ignore_index get loss = g = 0.
+ * library's exp (the clip written so that a NaN r stays NaN).  Rows with
+ * y == ignore_index get loss = g = 0; a NaN logp (a target outside the
+ * vocabulary) gives NaN loss and g.
  *   logp, logp_old, adv   fp32 [T]   (logp from rlk_linear_logp_fwd)
  *   logp_ref              fp32 [T]   reference policy; may be NULL if beta == 0
  *   loss, g               fp32 [T] out; either may be NULL
@@ -236,6 +238,22 @@ rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const flo
                              const float* logp_ref, const int32_t* y, int64_t T,
                              int32_t ignore_index, float eps_low, float eps_high, float beta,
                              float scale, float* loss, float* g, void* stream);
+
+/* The forward with the per-token RL objective fused into its last kernel
+ * (the pages' Roadmap lists RL loss fragments among the operator's next
+ * pieces; "Announcing RL-Kernel for vime", section "Roadmap"): logp and
+ * lse exactly as rlk_linear_logp_fwd, and loss and g exactly as
+ * rlk_rl_token_loss would compute them from that logp (the same function
+ * on the same fp32 value, so the same bits), without the extra launch and
+ * without reading logp back.  The objective's arguments and their checks
+ * are those of rlk_rl_token_loss; rows with y == ignore_index get
+ * logp = lse = loss = g = 0.  loss or g may be NULL, not both. */
+rlk_status rlk_linear_logp_fwd_rl(const void* h, const void* W, const int32_t* y,
+                                  int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                                  const float* logp_old, const float* adv, const float* logp_ref,
+                                  float eps_low, float eps_high, float beta, float scale,
+                                  float* logp, float* lse, float* loss, float* g,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* The forward without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,

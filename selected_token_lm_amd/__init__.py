@@ -13,6 +13,7 @@ library is missing or the device is not gfx950, calls raise.
     logp, lse = lse_merge(torch.stack(parts), y)
     C = gemm_bf16_nt(A, B)                  # deterministic A @ B^T
     logp, lse, z = linear_logp_fwd_save(h, W, y)          # save-logits variant
+    logp, lse, loss, g = linear_logp_fwd_rl(h, W, y, logp_old, adv)  # + RL objective
     grad_h, grad_W = linear_logp_bwd_saved(h, W, y, lse, g, z)
 """
 from __future__ import annotations
@@ -27,7 +28,7 @@ __all__ = [
     "workspace_bytes", "linear_logp_fwd", "linear_logp_bwd", "lse_partial",
     "lse_merge", "linear_logp", "gemm_bf16_nt", "linear_logp_fwd_save", "linear_logp_bwd_saved",
     "saved_logits_ld", "rl_token_loss", "profile_begin", "profile_end",
-    "linear_logp_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "linear_logp_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "linear_logp_fwd_rl",
 ]
 
 IGNORE_INDEX = -100
@@ -69,6 +70,11 @@ _SIGNATURES = {
                                  _c_void_p, _c_void_p, _c_void_p]),
     "rlk_linear_logp_fwd_noalloc": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
                                            _c_void_p, _c_void_p, _c_void_p]),
+    "rlk_linear_logp_fwd_rl": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                                      _c_void_p, _c_void_p, _c_void_p,
+                                      ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size,
+                                      _c_void_p]),
     # benchmark helpers (include/rlk_bench.h)
     "rlk_bench_mfma_ceiling": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p]),
     "rlk_profile_begin": (_i32, []),
@@ -159,8 +165,7 @@ def _rows(T, device, **named):
     for name, t in named.items():
         if not t.is_cuda or t.device != device:
             raise ValueError(f"{name} must be on {device}")
-    out = [t.to(torch.int32 if name == "y" else torch.float32).contiguous() for name, t in named.items()]
-    return out if len(out) > 1 else out[0]
+    return [t.to(torch.int32 if name == "y" else torch.float32).contiguous() for name, t in named.items()]
 
 
 def _workspace(op, T, H, V, device):
@@ -324,7 +329,7 @@ def lse_merge(parts, y, ignore_index: int = IGNORE_INDEX):
         raise ValueError("parts must be a device tensor")
     parts = parts.contiguous()
     P, T = parts.shape[0], parts.shape[1]
-    y = _rows(T, parts.device, y=y)
+    y, = _rows(T, parts.device, y=y)
     logp = torch.empty(T, dtype=torch.float32, device=parts.device)
     lse = torch.empty(T, dtype=torch.float32, device=parts.device)
     _check(lib().rlk_lse_merge(_ptr(parts), P, _ptr(y), T, ignore_index, _ptr(logp), _ptr(lse),
@@ -355,6 +360,34 @@ def gemm_bf16_nt(A, B, out_dtype=torch.float32):
                                   0 if out_dtype == torch.float32 else 1, _stream()),
            "rlk_gemm_bf16_nt")
     return C[:, :N] if ldc != N else C
+
+
+def linear_logp_fwd_rl(h, W, y, logp_old, adv, eps_low: float = 0.2, eps_high: float = 0.2,
+                       beta: float = 0.0, logp_ref=None, scale: float = 1.0,
+                       ignore_index: int = IGNORE_INDEX, ws=None):
+    """Forward with the per-token RL objective fused into its last kernel:
+    (logp, lse, loss, g), each fp32 [T]; logp/lse equal linear_logp_fwd's
+    bits and loss/g equal rl_token_loss's on that logp."""
+    h, W, y = _prep(h, W, y)
+    T, H = h.shape
+    V = W.shape[0]
+    if beta != 0.0 and logp_ref is None:
+        raise ValueError("logp_ref is required when beta != 0")
+    named = dict(logp_old=logp_old, adv=adv)
+    if logp_ref is not None:
+        named["logp_ref"] = logp_ref
+    checked = dict(zip(named, _rows(T, h.device, **named)))
+    out = [torch.empty(T, dtype=torch.float32, device=h.device) for _ in range(4)]
+    if ws is None:
+        ws, n = _workspace(OP_FWD, T, H, V, h.device)
+    else:
+        ws, n = _given_workspace(ws, h.device)
+    _check(lib().rlk_linear_logp_fwd_rl(_ptr(h), _ptr(W), _ptr(y), T, H, V, ignore_index,
+                                        _ptr(checked["logp_old"]), _ptr(checked["adv"]),
+                                        _ptr(checked.get("logp_ref")), eps_low, eps_high, beta, scale,
+                                        *(_ptr(t) for t in out), _ptr(ws), n, _stream()),
+           "rlk_linear_logp_fwd_rl")
+    return tuple(out)
 
 
 def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float = 0.2,

@@ -305,7 +305,7 @@ rlk_status split_range(int64_t vocab_start, int64_t vocab_len, int64_t V_global,
 rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V_global,
                        int32_t ignore_index, int s0, int nsplit, int64_t vocab_start, int64_t vocab_len, int mode,
                        float* logp, float* lse, rlk_lse_partial_t* pout, void* ws, hipStream_t st,
-                       float* zsave = nullptr, int64_t ldzs = 0) {
+                       float* zsave = nullptr, int64_t ldzs = 0, const rlk::RlLossArgs* rl = nullptr) {
   const Geom g = geom_of(V_global);
   const FwdWs L = fwd_layout(T, H, V_global);
   char* base = static_cast<char*>(ws);
@@ -318,7 +318,8 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   rlk::PartialRec* pr = reinterpret_cast<rlk::PartialRec*>(pout);
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, yA, n_act,
-             mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr);
+             mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr,
+             rl ? rl->loss : nullptr, rl ? rl->g : nullptr);
   RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, static_cast<const uint16_t*>(h), idx, n_act,
              (int)H, (int)V_global, y, nullptr, nullptr, hA, nullptr);
 
@@ -359,8 +360,10 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   else if (skinny == 3) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 3>), grid, block, st, fa);
   else RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 0>), grid, block, st, fa);
 
+  rlk::RlLossArgs rla{};  // no fused objective unless rl is given
+  if (rl) rla = *rl;
   RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, 64)), dim3(64 * rlk::kMergeWaves), st, rec, (size_t)T, zt, idx, n_act, y, gm,
-             nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr);
+             nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr, rla);
   return RLK_OK;
 }
 
@@ -477,7 +480,7 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
   const uint16_t* Wb = static_cast<const uint16_t*>(W);
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, nullptr, n_act, nullptr, nullptr,
-             nullptr);
+             nullptr, nullptr, nullptr);
   RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, (int)V, y, lse, g, hA,
              rowinfo);
   if (grad_h) {
@@ -636,15 +639,28 @@ rlk_status rlk_gemm_bf16_nt(const void* A, const void* B, int64_t M, int64_t N, 
   return ok();
 }
 
-rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const float* adv, const float* logp_ref,
-                             const int32_t* y, int64_t T, int32_t ignore_index, float eps_low, float eps_high,
-                             float beta, float scale, float* loss, float* g, void* stream) {
+namespace {
+
+// Host checks of the RL objective's arguments (shared by the standalone
+// call and the fused forward).
+rlk_status check_rl_args(int64_t T, const float* logp_old, const float* adv, const float* logp_ref, float eps_low,
+                         float eps_high, float beta, float scale) {
   if (T < 0 || T > kMaxT) return fail(RLK_ERR_BAD_SHAPE, "T=%lld out of [0, 2^24]", (long long)T);
   if (!(eps_low >= 0.f && eps_low < 1.f) || !(eps_high >= 0.f) || !(beta >= 0.f) || !(scale == scale))
     return fail(RLK_ERR_BAD_ARG, "need 0 <= eps_low < 1, eps_high >= 0, beta >= 0, scale not NaN");
+  if (T > 0 && (!logp_old || !adv || (beta != 0.f && !logp_ref)))
+    return fail(RLK_ERR_NULL_ARG, "logp_old, adv (and logp_ref when beta > 0) are required");
+  return RLK_OK;
+}
+
+}  // namespace
+
+rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const float* adv, const float* logp_ref,
+                             const int32_t* y, int64_t T, int32_t ignore_index, float eps_low, float eps_high,
+                             float beta, float scale, float* loss, float* g, void* stream) {
+  RLK_TRY(check_rl_args(T, logp_old, adv, logp_ref, eps_low, eps_high, beta, scale));
   if (T == 0) return ok();
-  if (!logp || !logp_old || !adv || !y || (beta != 0.f && !logp_ref))
-    return fail(RLK_ERR_NULL_ARG, "logp, logp_old, adv, y (and logp_ref when beta > 0) are required");
+  if (!logp || !y) return fail(RLK_ERR_NULL_ARG, "logp and y are required");
   if (!loss && !g) return ok();
   RLK_TRY(check_device());
   rlk::RlLossArgs ra;
@@ -662,6 +678,39 @@ rlk_status rlk_rl_token_loss(const float* logp, const float* logp_old, const flo
   ra.loss = loss;
   ra.g = g;
   RLK_LAUNCH(rl_token_loss, dim3((unsigned)ceil_div(T, 256)), dim3(256), static_cast<hipStream_t>(stream), ra);
+  return ok();
+}
+
+rlk_status rlk_linear_logp_fwd_rl(const void* h, const void* W, const int32_t* y, int64_t T, int64_t H, int64_t V,
+                                  int32_t ignore_index, const float* logp_old, const float* adv,
+                                  const float* logp_ref, float eps_low, float eps_high, float beta, float scale,
+                                  float* logp, float* lse, float* loss, float* g, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  RLK_TRY(check_common(h, W, y, T, H, V));
+  RLK_TRY(check_rl_args(T, logp_old, adv, logp_ref, eps_low, eps_high, beta, scale));
+  if (T == 0) return ok();
+  if (!logp || !ws || (!loss && !g)) return fail(RLK_ERR_NULL_ARG, "logp, ws and loss or g are required");
+  if (!aligned16(logp) || (lse && !aligned16(lse)) || !aligned16(ws))
+    return fail(RLK_ERR_BAD_ALIGNMENT, "logp, lse, ws must be 16-byte aligned");
+  if (ws_bytes < fwd_layout(T, H, V).total)
+    return fail(RLK_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", fwd_layout(T, H, V).total, ws_bytes);
+  RLK_TRY(check_device());
+  rlk::RlLossArgs ra;
+  ra.logp = logp;
+  ra.logp_old = logp_old;
+  ra.adv = adv;
+  ra.logp_ref = logp_ref;
+  ra.y = y;
+  ra.T = (int)T;
+  ra.ignore_index = ignore_index;
+  ra.eps_low = eps_low;
+  ra.eps_high = eps_high;
+  ra.beta = beta;
+  ra.scale = scale;
+  ra.loss = loss;
+  ra.g = g;
+  RLK_TRY(run_forward(h, W, y, T, H, V, ignore_index, 0, rlk::kNSplit, 0, V, 0, logp, lse, nullptr, ws,
+                      static_cast<hipStream_t>(stream), nullptr, 0, &ra));
   return ok();
 }
 

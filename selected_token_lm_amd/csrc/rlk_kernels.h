@@ -23,11 +23,54 @@
 namespace rlk {
 
 // ---------------------------------------------------------------------------
+// Per-token RL objective on the selected logp (PPO / GRPO clipped surrogate
+// and k3 KL to a reference), with its derivative g = dL/dlogp ready for the
+// backward.  Every operation is a separately rounded fp32 operation in the
+// order written; exp is the library's e(x).  One function for the
+// standalone kernel and the forward's fused epilogue (the same bits).
+// ---------------------------------------------------------------------------
+struct RlLossArgs {
+  const float* logp;
+  const float* logp_old;
+  const float* adv;
+  const float* logp_ref;  // may be NULL when beta == 0
+  const int32_t* y;
+  int T;
+  int ignore_index;
+  float eps_low, eps_high, beta, scale;
+  float* loss;  // may be NULL
+  float* g;     // may be NULL
+};
+
+// Loss and dL/dlogp of one active token t with selected log-probability lp.
+__device__ __forceinline__ void rl_token(const RlLossArgs& a, int t, float lp, float& L, float& gt) {
+  const float A = a.adv[t];
+  const float r = rlk_exp(lp - a.logp_old[t]);
+  // clip written with comparisons so that a NaN ratio (a row whose logp is
+  // NaN: its target lies outside the vocabulary) stays NaN; for every other
+  // value this is min(max(r, 1 - eps_low), 1 + eps_high)
+  const float lo = 1.f - a.eps_low, hi = 1.f + a.eps_high;
+  const float c = r < lo ? lo : (r > hi ? hi : r);
+  const float ra = r * A, ca = c * A;
+  L = -fminf(ra, ca);
+  gt = (ra <= ca) ? -ra : ((ra > ca) ? 0.f : ra);  // unordered (NaN): NaN
+  if (a.beta != 0.f) {
+    const float d = a.logp_ref[t] - lp;
+    const float ed = rlk_exp(d);
+    L = L + a.beta * ((ed - d) - 1.f);
+    gt = gt + a.beta * (1.f - ed);
+  }
+  L = a.scale * L;
+  gt = a.scale * gt;
+}
+
+// ---------------------------------------------------------------------------
 // Active-row compaction.  One block of 1024 threads scans y in order, so the
 // list is the active rows in ascending order and independent of timing;
 // yA (optional) receives their targets in the same order.
 // Inactive rows get their final outputs here: logp = lse = 0 (forward) or
-// the empty statistics {-inf, 0, 0, 0} (range partial).
+// the empty statistics {-inf, 0, 0, 0} (range partial), and loss = g = 0
+// when the forward also evaluates the RL objective.
 // ---------------------------------------------------------------------------
 struct PartialRec {
   float m, s, z_target;
@@ -38,7 +81,8 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
                                                      int32_t* __restrict__ idx, int32_t* __restrict__ yA,
                                                      int32_t* __restrict__ n_act,
                                                      float* __restrict__ logp, float* __restrict__ lse,
-                                                     PartialRec* __restrict__ pout) {
+                                                     PartialRec* __restrict__ pout, float* __restrict__ rl_loss,
+                                                     float* __restrict__ rl_g) {
   __shared__ int wave_tot[16];
   __shared__ int base_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -52,6 +96,8 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
       if (logp) logp[t] = 0.f;
       if (lse) lse[t] = 0.f;
       if (pout) pout[t] = PartialRec{-INFINITY, 0.f, 0.f, 0u};
+      if (rl_loss) rl_loss[t] = 0.f;
+      if (rl_g) rl_g[t] = 0.f;
     }
     const uint64_t bal = __ballot(act);
     const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
@@ -331,7 +377,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // wave w folds splits w, w+16 of the range (chunks left to right), the
 // split statistics meet in LDS and one thread per row runs the pairwise
 // tree over the nsplit splits.
-// mode 0 (forward):  logp[t] = (z_t - m) - log s, lse[t] = m + log s
+// mode 0 (forward):  logp[t] = (z_t - m) - log s, lse[t] = m + log s, and
+//                    when rl.loss or rl.g is set the per-token RL objective
+//                    of that logp (rl_token: the same bits as rl_token_loss)
 // mode 1 (partial):  pout[t] = {m, s, owned ? z_t : 0, owned}
 // ---------------------------------------------------------------------------
 constexpr int kMergeWaves = 16;  // waves of merge_splits (64 rows per block)
@@ -340,7 +388,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
                                                     const int32_t* __restrict__ n_act_p,
                                                     const int32_t* __restrict__ y, SplitGeom gm, int nsplit, int mode,
                                                     int own_lo, int own_hi, float* __restrict__ logp,
-                                                    float* __restrict__ lse, PartialRec* __restrict__ pout) {
+                                                    float* __restrict__ lse, PartialRec* __restrict__ pout,
+                                                    RlLossArgs rl) {
   __shared__ MS red[kNSplit][64];
   const int n_act = *n_act_p;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -389,8 +438,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
   if (mode == 0) {
     const float L = rlk_log(tot.s);
     const bool ok = yt >= 0 && yt < gm.V;
-    logp[t] = ok ? (zt[i] - tot.m) - L : __builtin_nanf("");
+    const float lp = ok ? (zt[i] - tot.m) - L : __builtin_nanf("");
+    logp[t] = lp;
     if (lse) lse[t] = tot.m + L;
+    if (rl.loss || rl.g) {
+      // the RL objective on this token's log-probability, as rl_token_loss
+      // computes it from the stored value
+      float loss, gt;
+      rl_token(rl, t, lp, loss, gt);
+      if (rl.loss) rl.loss[t] = loss;
+      if (rl.g) rl.g[t] = gt;
+    }
   } else {
     const bool owned = yt >= own_lo && yt < own_hi;
     pout[t] = PartialRec{tot.m, tot.s, owned ? zt[i] : 0.f, owned ? 1u : 0u};
@@ -863,45 +921,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 }
 
 
-// ---------------------------------------------------------------------------
-// Per-token RL objective on the selected logp (PPO / GRPO clipped surrogate
-// and k3 KL to a reference), with its derivative g = dL/dlogp ready for the
-// backward.  Every operation is a separately rounded fp32 operation in the
-// order written; exp is the library's e(x).  One thread per token.
-// ---------------------------------------------------------------------------
-struct RlLossArgs {
-  const float* logp;
-  const float* logp_old;
-  const float* adv;
-  const float* logp_ref;  // may be NULL when beta == 0
-  const int32_t* y;
-  int T;
-  int ignore_index;
-  float eps_low, eps_high, beta, scale;
-  float* loss;  // may be NULL
-  float* g;     // may be NULL
-};
-
+// Standalone per-token objective (rlk_rl_token_loss).  One thread per token.
 __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.T) return;
   float L = 0.f, gt = 0.f;
-  if (a.y[t] != a.ignore_index) {
-    const float lp = a.logp[t], A = a.adv[t];
-    const float r = rlk_exp(lp - a.logp_old[t]);
-    const float c = fminf(fmaxf(r, 1.f - a.eps_low), 1.f + a.eps_high);
-    const float ra = r * A, ca = c * A;
-    L = -fminf(ra, ca);
-    gt = (ra <= ca) ? -ra : 0.f;
-    if (a.beta != 0.f) {
-      const float d = a.logp_ref[t] - lp;
-      const float ed = rlk_exp(d);
-      L = L + a.beta * ((ed - d) - 1.f);
-      gt = gt + a.beta * (1.f - ed);
-    }
-    L = a.scale * L;
-    gt = a.scale * gt;
-  }
+  if (a.y[t] != a.ignore_index) rl_token(a, t, a.logp[t], L, gt);
   if (a.loss) a.loss[t] = L;
   if (a.g) a.g[t] = gt;
 }

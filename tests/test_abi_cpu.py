@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     # the benchmark helpers live in their own header, apart from the operator's ABI
     bench = declared_functions([os.path.join(ROOT, "include", "rlk_bench.h")])
     assert bench == ["rlk_bench_mfma_ceiling", "rlk_profile_begin", "rlk_profile_end"], bench
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(rlk._SIGNATURES)
@@ -244,3 +244,22 @@ def test_noalloc_validation():
     assert rlk.workspace_bytes(0, 4096, 4096, 151936) > rlk.NOALLOC_SCRATCH_BYTES
     assert call(T=4096, H=4096, V=151936) == WS_SMALL
     assert b"fixed device scratch" in L.rlk_last_error_message()
+
+
+def test_fused_rl_forward_validation():
+    L = rlk.lib()
+
+    def call(T=64, H=256, V=4096, old=FAKE, adv=FAKE, ref=None, eps_lo=0.2, beta=0.0, logp=FAKE, loss=FAKE,
+             g=FAKE, nbytes=1 << 40):
+        return L.rlk_linear_logp_fwd_rl(FAKE, FAKE, FAKE, T, H, V, -100, old, adv, ref, eps_lo, 0.2, beta, 1.0,
+                                        logp, FAKE, loss, g, FAKE, nbytes, None)
+
+    assert call(old=None) == NULL_ARG
+    assert call(adv=None) == NULL_ARG
+    assert call(beta=0.1) == NULL_ARG          # logp_ref is required with a KL term
+    assert call(eps_lo=1.0) == BAD_ARG
+    assert call(beta=-1.0) == BAD_ARG
+    assert call(loss=None, g=None) == NULL_ARG
+    assert call(H=96) == BAD_SHAPE
+    assert call(nbytes=10) == WS_SMALL
+    assert call(T=0, old=None, adv=None, logp=None, loss=None, g=None) == OK

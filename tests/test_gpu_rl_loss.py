@@ -92,3 +92,33 @@ def test_end_to_end_gradients():
     say(f"  end to end: loss sum {to64(loss).sum():.6f} vs {o_loss.sum():.6f}; rel L2 grad_h {e_h:.2e} grad_W {e_W:.2e}")
     assert abs(to64(loss).sum() - o_loss.sum()) <= 1e-4 * (1 + abs(o_loss.sum()))
     assert e_h <= GRAD_RTOL and e_W <= GRAD_RTOL
+
+
+@pytest.mark.parametrize("T,H,V,beta", [(700, 256, 30000, 0.0), (700, 256, 30000, 0.05), (1, 64, 5003, 0.1),
+                                        (129, 128, 257, 0.0)])
+def test_fused_forward_objective_bitwise_equal_to_separate_calls(T, H, V, beta):
+    """rlk_linear_logp_fwd_rl: logp and lse bit-equal to the forward, loss and
+    g bit-equal to rlk_rl_token_loss on that logp (the same per-token function
+    inside the forward's merge kernel); masked rows 0; an out-of-range target
+    gives NaN through both paths."""
+    inp = synth.make_inputs(T, H, V, 0.15)
+    if T > 5:
+        inp.y[5] = V  # out of range: NaN logp, NaN objective
+    h, W, y, _ = dev_inputs(inp)
+    gen = np.random.Generator(np.random.PCG64(T))
+    ref_lp, _ = rlk.linear_logp_fwd(h, W, y)
+    old = ref_lp + f32_dev(gen.normal(0, 0.3, T).astype(np.float32))
+    adv = f32_dev(gen.normal(0, 1, T).astype(np.float32))
+    lref = ref_lp + f32_dev(gen.normal(0, 0.2, T).astype(np.float32)) if beta else None
+    say(f"[rl fused] T={T} H={H} V={V} beta={beta}")
+    lp, lse, loss, g = rlk.linear_logp_fwd_rl(h, W, y, old, adv, 0.2, 0.28, beta, lref, 1.0 / T)
+    ref_lp2, ref_lse = rlk.linear_logp_fwd(h, W, y)
+    ref_loss, ref_g = rlk.rl_token_loss(ref_lp2, old, adv, y, 0.2, 0.28, beta, lref, 1.0 / T)
+    torch.cuda.synchronize()
+    for a, b in ((lp, ref_lp2), (lse, ref_lse), (loss, ref_loss), (g, ref_g)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    masked = torch.from_numpy(inp.y == -100).to(DEV)
+    assert torch.all(loss[masked] == 0) and torch.all(g[masked] == 0)
+    if T > 5:
+        # no silent finite objective for a row without a log-probability
+        assert torch.isnan(loss[5]) and torch.isnan(g[5])
