@@ -512,11 +512,16 @@ __device__ __forceinline__ int xcd_tile(int live, int bid) {
 
 // Tile id -> (fast index f < F, slow index c < C) in groups of GM fast
 // indices: consecutive ids walk the GM values of f of a group, then the
-// next c.  With GM = min(8, F) the ~32 tiles an XCD runs together (its
+// next c.  With GM near 8 the ~32 tiles an XCD runs together (its
 // contiguous id range, see xcd_tile) form an 8 x 4 block whose 12 operand
 // tiles per k-block are shared in its L2 (measured best among group sizes
-// 4..16, on the LM-head and on square products).
-__device__ __forceinline__ int row_group(int F) { return min(8, F); }
+// 4..16, on the LM-head and on square products).  row_group splits F into
+// ceil(F / 8) groups of equal size (14 row tiles: two groups of 7, not 8 +
+// 6), so that the XCD ranges do not straddle a short last group.
+__device__ __forceinline__ int row_group(int F) {
+  const int ng = (F + 7) >> 3;
+  return (F + ng - 1) / ng;
+}
 __device__ __forceinline__ void grouped_tile(int id, int F, int& f, int& c, int C, int GM) {
   const int per_group = GM * C;
   const int grp = id / per_group;

@@ -750,10 +750,14 @@ struct GradWArgs {
 
 // grad_W rows of the group's splits: C[v][n] = sum_t dz[t][v] h[t][n], the
 // chain over active rows t ascending (K padded to 64 with zero dz rows).
-// Both operands are MN mode.  Written once, fp32.  Tile id: (H tile, v tile).
+// Both operands are MN mode.  Written once, fp32.  Tile id: (H tile, v tile),
+// in groups of 4 H tiles: an XCD's ~32 running tiles are then 4 H tiles x 8
+// v tiles, and the h columns it keeps re-reading (4 tiles of all active
+// rows) stay small (measured against groups of 2, 8 and 16: the fastest).
+constexpr int kGradWGroup = 4;
 __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4* lds) {
   int nt, vt;
-  grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps, row_group(a.n_tiles));
+  grouped_tile(id, a.n_tiles, nt, vt, a.bg.G * a.tps, min(kGradWGroup, a.n_tiles));
   const int sc = vt / a.tps, j = vt - sc * a.tps;
   const int sbeg = (a.bg.c_lo + sc) * a.gm.S;
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));
