@@ -87,22 +87,30 @@ def _elf_sections(data):
     return {names[s[0]:names.index(b"\0", s[0])].decode(): (s[3], data[s[4]:s[4] + s[5]]) for s in sec}
 
 
-def _gfx950_code_object(lib_path):
-    """The gfx950 code object (an ELF image) inside the library's offload bundle."""
+def _gfx950_code_objects(lib_path):
+    """The gfx950 code objects (ELF images) inside the library's offload
+    bundles, one per translation unit (the .hip_fatbin section holds the
+    bundles one after another)."""
     import struct
     with open(lib_path, "rb") as f:
-        bundle = _elf_sections(f.read())[".hip_fatbin"][1]
+        section = _elf_sections(f.read())[".hip_fatbin"][1]
     magic = b"__CLANG_OFFLOAD_BUNDLE__"
-    assert bundle.startswith(magic), "uncompressed offload bundle expected"
-    n, = struct.unpack_from("<Q", bundle, len(magic))
-    pos = len(magic) + 8
-    for _ in range(n):
-        off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
-        triple = bundle[pos + 24:pos + 24 + tlen].decode()
-        pos += 24 + tlen
-        if "gfx950" in triple:
-            return bundle[off:off + size]
-    raise KeyError("gfx950")
+    assert section.startswith(magic), "uncompressed offload bundle expected"
+    found, start = [], 0
+    while start >= 0:
+        bundle = section[start:]
+        n, = struct.unpack_from("<Q", bundle, len(magic))
+        pos = len(magic) + 8
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", bundle, pos)
+            triple = bundle[pos + 24:pos + 24 + tlen].decode()
+            pos += 24 + tlen
+            if "gfx950" in triple:
+                found.append(bundle[off:off + size])
+        start = section.find(magic, start + len(magic))
+    if not found:
+        raise KeyError("gfx950")
+    return found
 
 
 def kernel_digest(kernel):
@@ -111,18 +119,18 @@ def kernel_digest(kernel):
     does, whatever else changes in the sources."""
     import struct
     import selected_token_lm_amd as rlk
-    co = _gfx950_code_object(rlk.library_path)
-    secs = _elf_sections(co)
-    text_addr, text = secs[".text"]
-    strtab = secs[".strtab"][1]
-    symtab = secs[".symtab"][1]
     h = hashlib.sha256()
     found = []
-    for i in range(0, len(symtab), 24):
-        name_off, info, _, _, value, size = struct.unpack_from("<IBBHQQ", symtab, i)
-        name = strtab[name_off:strtab.index(b"\0", name_off)].decode()
-        if (info & 0xF) == 2 and size and f"{len(kernel)}{kernel}" in name:  # STT_FUNC, mangled name
-            found.append((name, text[value - text_addr:value - text_addr + size]))
+    for co in _gfx950_code_objects(rlk.library_path):
+        secs = _elf_sections(co)
+        text_addr, text = secs[".text"]
+        strtab = secs[".strtab"][1]
+        symtab = secs[".symtab"][1]
+        for i in range(0, len(symtab), 24):
+            name_off, info, _, _, value, size = struct.unpack_from("<IBBHQQ", symtab, i)
+            name = strtab[name_off:strtab.index(b"\0", name_off)].decode()
+            if (info & 0xF) == 2 and size and f"{len(kernel)}{kernel}" in name:  # STT_FUNC, mangled name
+                found.append((name, text[value - text_addr:value - text_addr + size]))
     for name, code in sorted(found):
         h.update(name.encode() + code)
     return h.hexdigest()[:16] if found else None

@@ -16,6 +16,7 @@
 #include "rlk.h"
 #include "rlk_bench.h"
 #include "rlk_kernels.h"
+#include "rlk_tiles_w8.h"
 
 namespace {
 
@@ -181,9 +182,10 @@ bool grad_h_passes(int64_t row_tiles, int64_t n_tiles) {
   return 3 * row_tiles * n_tiles <= device_cus();
 }
 
-// Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension.
+// Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension
+// (checked for the larger of the two block sizes).
 rlk_status check_grid(int64_t blocks) {
-  if (blocks * rlk::kThreads > (int64_t)UINT32_MAX)
+  if (blocks * std::max(rlk::kThreads, rlk::kThreadsW8) > (int64_t)UINT32_MAX)
     return fail(RLK_ERR_BAD_SHAPE, "problem needs %lld tile blocks, more than one launch holds", (long long)blocks);
   return RLK_OK;
 }
@@ -268,6 +270,17 @@ struct ProfScope {
       hipLaunchKernelGGL(fn, grid, block, 0, st, __VA_ARGS__);  \
     }                                                           \
     RLK_TRY(launched(name));                                    \
+  } while (0)
+
+// Same for a launch made by a launcher of the eight-wave unit
+// (rlk_tiles_w8.h), timed under `name`.
+#define RLK_LAUNCH_W8(name, launcher, grid, st, args) \
+  do {                                                \
+    {                                                 \
+      ProfScope _ps(name, st);                        \
+      rlk::launcher(grid, st, args);                  \
+    }                                                 \
+    RLK_TRY(launched(name));                          \
   } while (0)
 
 // Shapes first; with T == 0 there is nothing to read or write, so the
@@ -358,7 +371,7 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   else if (skinny == 1) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 1>), grid, block, st, fa);
   else if (skinny == 2) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 2>), grid, block, st, fa);
   else if (skinny == 3) RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 3>), grid, block, st, fa);
-  else RLK_LAUNCH_FN("fwd_tiles", (rlk::fwd_tiles<false, 0>), grid, block, st, fa);
+  else RLK_LAUNCH_W8("fwd_tiles", launch_fwd_tiles_w8, grid, st, fa);
 
   rlk::RlLossArgs rla{};  // no fused objective unless rl is given
   if (rl) rla = *rl;
@@ -528,7 +541,7 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
       RLK_LAUNCH(dz_saved, dim3((unsigned)ceil_div(bg.ldz / 8, 256), (unsigned)L.T_pad), dim3(256), st, zsave, ldzs,
                  idx, rowinfo, n_act, gm, bg, dZ);
     else
-      RLK_LAUNCH(dz_tiles, dim3((unsigned)dz_blocks), dim3(rlk::kThreads), st, da);
+      RLK_LAUNCH_W8("dz_tiles", launch_dz_tiles_w8, dim3((unsigned)dz_blocks), st, da);
 
     rlk::GradWArgs wa;
     wa.dZ = dZ;

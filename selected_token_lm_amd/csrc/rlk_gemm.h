@@ -47,7 +47,24 @@
 
 #include "rlk_device.h"
 
-namespace rlk {
+// The library is built from two translation units: rlk_api.hip compiles
+// the engine with RLK_WAVES waves per tile (4 by default) in namespace rlk,
+// and rlk_tiles_w8.hip compiles it with 8 waves (RLK_ENGINE_W8) in
+// rlk::w8, so that the two flavours' device functions and kernels have
+// distinct names in one library.
+#ifdef RLK_ENGINE_W8
+#define RLK_ENGINE_BEGIN \
+  namespace rlk {        \
+  inline namespace w8 {
+#define RLK_ENGINE_END \
+  }                    \
+  }
+#else
+#define RLK_ENGINE_BEGIN namespace rlk {
+#define RLK_ENGINE_END }
+#endif
+
+RLK_ENGINE_BEGIN
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // native 16-byte vector (HIP's uint4 is a struct, which keeps staging
@@ -59,6 +76,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kWaves = RLK_WAVES;
 static_assert(kWaves == 4 || kWaves == 8, "four or eight waves per tile");
+#ifdef RLK_ENGINE_W8
+static_assert(kWaves == 8, "the eight-wave unit");
+#endif
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 64 * kWaves;
 constexpr int kWM = kWaves / 2;            // waves along the tile's rows (two along its columns)
 constexpr int kWaveRows = kBM / kWM;       // tile rows per wave
@@ -531,4 +551,4 @@ __device__ __forceinline__ void grouped_tile(int id, int F, int& f, int& c, int 
   f = grp * GM + (within - c * gm);
 }
 
-}  // namespace rlk
+RLK_ENGINE_END  // namespace rlk

@@ -18,9 +18,14 @@
 //   gemm_tiles         C = A B^T, one MFMA chain per element
 #pragma once
 
+#include "rlk_args.h"
 #include "rlk_gemm.h"
 
-namespace rlk {
+// Which unit builds which kernel: the eight-wave unit (RLK_ENGINE_W8) the
+// plain forward's fwd_tiles instance and dz_tiles; the four-wave unit the
+// other fwd_tiles instances (save-logits, small batches), grad_tiles, the
+// dense product, the row kernels and the merges.
+RLK_ENGINE_BEGIN
 
 // ---------------------------------------------------------------------------
 // Per-token RL objective on the selected logp (PPO / GRPO clipped surrogate
@@ -29,19 +34,6 @@ namespace rlk {
 // order written; exp is the library's e(x).  One function for the
 // standalone kernel and the forward's fused epilogue (the same bits).
 // ---------------------------------------------------------------------------
-struct RlLossArgs {
-  const float* logp;
-  const float* logp_old;
-  const float* adv;
-  const float* logp_ref;  // may be NULL when beta == 0
-  const int32_t* y;
-  int T;
-  int ignore_index;
-  float eps_low, eps_high, beta, scale;
-  float* loss;  // may be NULL
-  float* g;     // may be NULL
-};
-
 // Loss and dL/dlogp of one active token t with selected log-probability lp.
 __device__ __forceinline__ void rl_token(const RlLossArgs& a, int t, float lp, float& L, float& gt) {
   const float A = a.adv[t];
@@ -72,11 +64,7 @@ __device__ __forceinline__ void rl_token(const RlLossArgs& a, int t, float lp, f
 // the empty statistics {-inf, 0, 0, 0} (range partial), and loss = g = 0
 // when the forward also evaluates the RL objective.
 // ---------------------------------------------------------------------------
-struct PartialRec {
-  float m, s, z_target;
-  uint32_t owned;
-};
-
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__ y, int T, int ignore_index,
                                                      int32_t* __restrict__ idx, int32_t* __restrict__ yA,
                                                      int32_t* __restrict__ n_act,
@@ -119,18 +107,11 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
   }
   if (tid == 0) *n_act = base_s;
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // Vocabulary geometry
 // ---------------------------------------------------------------------------
-struct SplitGeom {
-  int V;           // global vocabulary size
-  int S;           // split width = ceil(V / 32)
-  int cps;         // chunks per split = ceil(S / 128)
-  int s0;          // first split of the processed range
-  int vocab_start; // global index of row 0 of the W pointer given
-};
-
 __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, int& c1) {
   const int split = gm.s0 + g / gm.cps;
   const int j = g - (g / gm.cps) * gm.cps;
@@ -200,29 +181,6 @@ __device__ __forceinline__ float2 chunk_stats(const float (&v)[64]) {
   lane_halves(exp_tree<64>(v, 0, mx), lo, hi);
   return make_float2(mx, lo + hi);
 }
-
-struct TileGeom {
-  int tps;  // 256-column tiles per split = ceil(S / 256)
-};
-
-struct FwdArgs {
-  const uint16_t* hA;  // active rows of h, compacted, zero padded to a multiple of 256
-  const uint16_t* W;
-  const int32_t* yA;  // targets of the active rows, compacted
-  const int32_t* idx;
-  const int32_t* n_act;
-  int H;
-  int nsplit;
-  SplitGeom gm;
-  TileGeom tg;
-  size_t rec_stride;
-  float2* rec;
-  float* zt;
-  float* zsave;  // kSave: fp32 logits of active rows: row t, split s, column c of
-                 // the split at zsave + t * ldzs + s * zs_spad + c
-  int64_t ldzs;
-  int zs_spad;   // S rounded up to 64
-};
 
 // Engine call for a K-mode x K-mode tile.  kSkinny = 1..3 (four-wave
 // layout only): the caller guarantees that every valid row of the tile lies
@@ -383,6 +341,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // mode 1 (partial):  pout[t] = {m, s, owned ? z_t : 0, owned}
 // ---------------------------------------------------------------------------
 constexpr int kMergeWaves = 16;  // waves of merge_splits (64 rows per block)
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* __restrict__ rec, size_t rec_stride,
                                                     const float* __restrict__ zt, const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ n_act_p,
@@ -454,6 +413,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
     pout[t] = PartialRec{tot.m, tot.s, owned ? zt[i] : 0.f, owned ? 1u : 0u};
   }
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // rlk_lse_merge: per row, balanced tree over n_parts range statistics.
@@ -464,6 +424,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
 // subtrees reduce to exactly the unpadded ones.  (Every index is a
 // compile-time constant, so the 32 records stay in registers.)
 // ---------------------------------------------------------------------------
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict__ parts, int n_parts, int T,
                                                    const int32_t* __restrict__ y, int ignore_index,
                                                    float* __restrict__ logp, float* __restrict__ lse) {
@@ -499,6 +460,7 @@ __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict_
   logp[t] = (owners == 1) ? (z - acc.m) - L : __builtin_nanf("");
   if (lse) lse[t] = acc.m + L;
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // Backward.  The vocabulary splits are processed in groups of G consecutive
@@ -509,31 +471,12 @@ __global__ __launch_bounds__(256) void merge_parts(const PartialRec* __restrict_
 // rows and grad_h's chain runs over the vocabulary in ascending order with
 // the same zero padding after every split, whatever G is.
 // ---------------------------------------------------------------------------
-struct BwdGeom {
-  int c_lo;   // first split of the group
-  int G;      // splits in the group
-  int S_pad;  // S rounded up to 64
-  int ldz;    // G * S_pad
-  int T_pad;  // rows of dZ (multiple of 256)
-};
-
-struct DzArgs {
-  const uint16_t* hA;       // active rows of h, compacted, zero padded to T_pad
-  const uint16_t* W;
-  const float4* rowinfo;    // per active row {lse, g, target (bits), 0}; {0, 0, -1, 0} past n_act
-  const int32_t* n_act;
-  int H;
-  SplitGeom gm;
-  TileGeom tg;
-  BwdGeom bg;
-  uint16_t* dZ;
-};
-
 // dz for the group's splits on 256 x 256 tiles (same tiles and logits as the
 // forward): p = exp(z - lse_i), dz = g_i * ([v == y_i] - p) in fp32, rounded
 // once to bf16.  Rows >= n_act of the tile and columns >= the split's width
 // are written as zeros.  The tile is staged in LDS and stored row by row
 // (16 bytes per lane, whole 512-byte rows per instruction pair of lanes).
+#ifdef RLK_ENGINE_W8
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void dz_tiles(DzArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int n_act = __builtin_amdgcn_readfirstlane(*a.n_act);
@@ -637,12 +580,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
     }
   }
 }
+#endif
 
 // dz of the group from saved logits (the forward's kSave output, same split
 // layout as dZ) instead of a recomputed tile: the same z bits, primitives
 // and rounding as dz_tiles, so the same dz bits.  One thread per 8
 // consecutive dZ columns of one compacted row; grid (G * S_pad / 8 / 256,
 // T_pad); rows past the active row tiles are left alone (never read).
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void dz_saved(const float* __restrict__ zsave, int64_t ldzs,
                                                  const int32_t* __restrict__ idx, const float4* __restrict__ rowinfo,
                                                  const int32_t* __restrict__ n_act_p, SplitGeom gm, BwdGeom bg,
@@ -682,6 +627,7 @@ __global__ __launch_bounds__(256) void dz_saved(const float* __restrict__ zsave,
   *reinterpret_cast<u32x4*>(dZ + (size_t)i * bg.ldz + col0) =
       u32x4{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])};
 }
+#endif
 
 // MN-mode loader over a row-major matrix: k-row t of k-block kt is matrix
 // row kBK kt + t at this tile's columns (dz columns for grad_W's A operand,
@@ -736,18 +682,6 @@ struct WRowsMN {
   }
 };
 
-struct GradWArgs {
-  const uint16_t* dZ;
-  const uint16_t* hA;  // active rows of h, compacted, zero padded to T_pad
-  const int32_t* n_act;
-  int H;
-  SplitGeom gm;
-  BwdGeom bg;
-  int tps;      // 256-row v tiles per split
-  int n_tiles;  // 256-column tiles of H
-  float* grad_W;  // NULL: not wanted
-};
-
 // grad_W rows of the group's splits: C[v][n] = sum_t dz[t][v] h[t][n], the
 // chain over active rows t ascending (K padded to 64 with zero dz rows).
 // Both operands are MN mode.  Written once, fp32.  Tile id: (H tile, v tile),
@@ -788,19 +722,6 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
       }
   }
 }
-
-struct GradHArgs {
-  const uint16_t* dZ;
-  const uint16_t* W;
-  const int32_t* idx;
-  const int32_t* n_act;
-  int H;
-  SplitGeom gm;
-  BwdGeom bg;
-  int n_tiles;  // 256-column tiles of H
-  float* ghacc;
-  uint16_t* grad_h;  // NULL: not wanted
-};
 
 // grad_h of the group: acc[i][n] (+)= sum_v dz[i][v] W[v][n] over the
 // group's padded columns.  A (dz rows) is K mode, B (W rows) MN mode.  The
@@ -926,6 +847,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 
 
 // Standalone per-token objective (rlk_rl_token_loss).  One thread per token.
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.T) return;
@@ -934,6 +856,7 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
   if (a.loss) a.loss[t] = L;
   if (a.g) a.g[t] = gt;
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // Benchmark only: the MFMA ceiling of the part under realistic operands.
@@ -943,6 +866,7 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
 // matrix cores see realistic bit toggling; no memory traffic in the loop.
 // src: 32 * 256 16-byte pieces; out: one float per thread (keeps the result).
 // ---------------------------------------------------------------------------
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ceiling(
     const u32x4* __restrict__ src, float* __restrict__ out, int iters) {
   bf16x8 fa[4][4], fb[4][4];  // [set][fragment]
@@ -969,6 +893,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < 16; ++i) t += c[j][i];
   out[blockIdx.x * 256 + threadIdx.x] = t;
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // Deterministic dense product C = A B^T on the same tile engine: every
@@ -977,16 +902,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // A, row tile of B).  Rows past M / N are clamped loads that are never
 // stored.  c_bf16: store bf16 (round to nearest even, once) instead of fp32.
 // ---------------------------------------------------------------------------
-struct GemmArgs {
-  const uint16_t* A;  // [M, K]
-  const uint16_t* B;  // [N, K]
-  int M, N, K;
-  int rtiles, ctiles;
-  int64_t ldc;
-  int c_bf16;
-  void* C;
-};
-
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WAVES / 4, RLK_WAVES / 4))) void gemm_tiles(GemmArgs a) {
   __shared__ u32x4 lds[kLdsU4];
   const int id = xcd_tile(a.rtiles * a.ctiles, blockIdx.x);
@@ -1034,6 +950,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
       }
   }
 }
+#endif
 
 
 // hA[i] = h[idx[i]] for active rows i < n_act, zero rows for n_act <= i <
@@ -1043,6 +960,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // so that the backward's gradients show it (NaN in the row's grad_h and in
 // every grad_W element it reaches) instead of silently dropping the target
 // term.  grid rows, block 256; 16-byte pieces.
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ n_act_p, int H, int V,
                                                    const int32_t* __restrict__ y, const float* __restrict__ lse,
@@ -1065,13 +983,16 @@ __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ 
     if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
   }
 }
+#endif
 
 // Zero the grad_h rows of inactive rows.  grid T, block 256.
+#ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void zero_rows(const int32_t* __restrict__ y, int ignore_index, int H,
                                                  uint16_t* __restrict__ grad_h) {
   const int t = blockIdx.x;
   if (y[t] != ignore_index) return;
   for (int k = threadIdx.x; k < H; k += 256) grad_h[(size_t)t * H + k] = 0;
 }
+#endif
 
-}  // namespace rlk
+RLK_ENGINE_END  // namespace rlk
