@@ -831,7 +831,7 @@ def main():
                     "2.4 GHz it assumes (clock_power)",
             "tflops": PEAK_BF16 / 1e12 * clock_power["gfx_clock_mhz"]["median"] / 2400.0,
             "dominant_kernel_frac": achieved / (PEAK_BF16 * clock_power["gfx_clock_mhz"]["median"] / 2400.0)},
-        "mfma_ceiling": {"what": "pure v_mfma_f32_32x32x16_bf16 loop on random bf16 operands, no memory traffic, "
+        "mfma_ceiling": {"what": "pure loop of the tile engine's MFMA instruction on random bf16 operands, no memory traffic, "
                                  "same box after the timed steps (rlk_bench_mfma_ceiling)",
                          "best_tflops": ceiling["best_tflops"], "median_tflops": ceiling["median_tflops"],
                          "dominant_kernel_frac_of_ceiling": achieved / 1e12 / ceiling["median_tflops"]},

@@ -17,12 +17,17 @@
  * section "The Numerical Execution Contract") but publish no constants; the
  * ones below are this library's own:
  *   - logits: bf16 x bf16 products accumulated in fp32 by one
- *     v_mfma_f32_32x32x16_bf16 chain per logit, k ascending in steps of 16;
+ *     v_mfma_f32_16x16x32_bf16 chain per logit, k ascending in steps of 32
+ *     (version 2; version 1, a build with RLK_MFMA=32, used
+ *     v_mfma_f32_32x32x16_bf16 in steps of 16, which gives other bits);
  *   - the vocabulary is split into 32 contiguous splits of width
  *     S = ceil(V_global / 32); each split into chunks of 128 columns anchored
  *     at the split start (the last chunk may be short);
  *   - chunk statistics (m, s): m = max of the chunk's logits, s = sum of
- *     exp(z - m) in a fixed lane order; chunks of a split are folded left to
+ *     exp(z - m) over the columns in four interleaved parts (column c in
+ *     part (c / 4) mod 4), each a balanced pairwise tree in ascending
+ *     column order, combined as (s0 + s1) + (s2 + s3) (version 1: two
+ *     parts, (c / 4) mod 2, s0 + s1); chunks of a split are folded left to
  *     right with the operator  (ma,sa) + (mb,sb) = (m, sa*e(ma-m) + sb*e(mb-m)),
  *     m = max(ma,mb); splits are merged with a balanced binary tree;
  *   - exp(x) = exp2(x * log2(e)) and log(x) = log2(x) * ln(2) on the
@@ -63,7 +68,9 @@
 extern "C" {
 #endif
 
-#define RLK_CONTRACT_VERSION 1
+/* The contract version of the default build; rlk_contract_version() returns
+ * the one the library was built with. */
+#define RLK_CONTRACT_VERSION 2
 #define RLK_NSPLIT 32
 #define RLK_CHUNK 128
 

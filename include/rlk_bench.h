@@ -18,11 +18,13 @@ extern "C" {
 #endif
 
 /* Benchmark only (computes nothing of the operator): runs `blocks`
- * workgroups of 4 waves, each wave issuing iters * 64
- * v_mfma_f32_32x32x16_bf16 on a 128 x 128 accumulator tile with operands
- * cycled through 4 register sets of random bf16 data, and no memory traffic
- * in the loop: the MFMA throughput the part sustains under its power limit
- * with realistic operand toggling (2 * 32 * 32 * 16 FLOP per instruction).
+ * workgroups of 4 waves, each wave issuing, per iteration, the tile engine's
+ * MFMA instruction on a 128 x 128 accumulator tile (128
+ * v_mfma_f32_16x16x32_bf16 over 2 register sets of operands; a contract-1
+ * build: 64 v_mfma_f32_32x32x16_bf16 over 4 sets), operands of random bf16
+ * data, and no memory traffic in the loop: the MFMA throughput the part
+ * sustains under its power limit with realistic operand toggling
+ * (2^21 FLOP per wave per iteration either way).
  *   src  bf16 device buffer of 32 * 256 * 8 values (random; 16-byte aligned)
  *   out  fp32 [blocks * 256] out (sums of the accumulators, so nothing is
  *        optimised away) */

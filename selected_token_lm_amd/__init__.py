@@ -417,8 +417,10 @@ def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float 
 
 
 def bench_mfma_ceiling(blocks: int = 256, iters: int = 4096, repeats: int = 3):
-    """Benchmark only: TFLOP/s of a pure v_mfma_f32_32x32x16_bf16 loop on random
-    operands (no memory traffic), best and median of `repeats` timed launches."""
+    """Benchmark only: TFLOP/s of a pure loop of the tile engine's MFMA
+    instruction (v_mfma_f32_16x16x32_bf16; v_mfma_f32_32x32x16_bf16 in a
+    contract-1 build) on random operands (no memory traffic), best and median
+    of `repeats` timed launches.  2^21 FLOP per wave per iteration."""
     gen = torch.Generator(device="cuda").manual_seed(12345)
     src = torch.randn(32 * 256 * 8, device="cuda", generator=gen).to(torch.bfloat16)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")

@@ -384,7 +384,9 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
 
 extern "C" {
 
-int32_t rlk_contract_version(void) { return RLK_CONTRACT_VERSION; }
+// Version 2: 16 x 16 x 32 MFMA steps (the default engine); 1: 32 x 32 x 16.
+int32_t rlk_contract_version(void) { return rlk::kBlk == 16 ? 2 : 1; }
+static_assert(rlk::kBlk != 16 || RLK_CONTRACT_VERSION == 2, "the default build implements the header's version");
 
 const char* rlk_status_string(rlk_status s) {
   switch (s) {

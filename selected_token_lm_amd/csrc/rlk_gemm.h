@@ -45,6 +45,8 @@
 // memory requests per byte compared with 32-wide k-blocks.
 #pragma once
 
+#include <utility>
+
 #include "rlk_device.h"
 
 // The library is built from two translation units: rlk_api.hip compiles
@@ -82,10 +84,23 @@ static_assert(kWaves == 8, "the eight-wave unit");
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 64 * kWaves;
 constexpr int kWM = kWaves / 2;            // waves along the tile's rows (two along its columns)
 constexpr int kWaveRows = kBM / kWM;       // tile rows per wave
-constexpr int kMI = kWaveRows / 32, kNI = 4;  // 32 x 32 blocks per wave
+// MFMA shape (RLK_MFMA at build time): 32 = v_mfma_f32_32x32x16_bf16
+// (32 x 32 blocks, 16 k per step; the default), 16 =
+// v_mfma_f32_16x16x32_bf16 (16 x 16 blocks, 32 k per step).  The shape is
+// part of the numerical contract: it fixes how many products each MFMA step
+// sums before the fp32 accumulation.
+#ifndef RLK_MFMA
+#define RLK_MFMA 16
+#endif
+constexpr int kBlk = RLK_MFMA;
+static_assert(kBlk == 16 || kBlk == 32, "16 x 16 x 32 or 32 x 32 x 16 MFMAs");
+constexpr int kKStep = 512 / kBlk;          // k summed per MFMA step: 32 or 16
+constexpr int kLPR = 64 / kBlk;             // lanes holding one row of a block: 4 or 2
+constexpr int kQL = kBlk * kBlk / 256;      // groups of 4 consecutive columns per lane per block: 1 or 4
+constexpr int kMI = kWaveRows / kBlk, kNI = 128 / kBlk;  // blocks per wave
 constexpr int kMma = kMI * kNI;            // MFMAs per wave per k step
 constexpr int kReads = kMI + kNI;          // fragment reads per wave per k step
-constexpr int kKK = kBK / 16;              // MFMA k steps per k-block
+constexpr int kKK = kBK / kKStep;          // MFMA k steps per k-block
 constexpr int kSegs = kBK / 8;             // 16-byte pieces per K-mode row
 constexpr int kTileU4 = 256 * kSegs;       // u32x4 per operand tile (32 KB)
 constexpr int kDma = kTileU4 / 64 / kWaves;  // direct-load instructions per wave per operand per k-block
@@ -112,34 +127,42 @@ __device__ __forceinline__ int wave_m(int w) { return w & (kWM - 1); }
 __device__ __forceinline__ int wave_n(int w) { return w >> (kWM == 2 ? 1 : 2); }
 
 // ---- operand fragments from LDS ----------------------------------------------
+// MFMA operand layout (both shapes, X and Y alike): lane l holds row
+// (l % kBlk) of the block and k = 8 (l / kBlk) .. +7 of the k step, so a
+// step sums exactly its kKStep k values.
+//
 // Per-lane LDS byte offsets of one operand's fragments within its tile,
 // computed once per tile so that every read in the main loop is a base
 // register plus an immediate:
-//   K mode : fragment J (rows r0 + 32 J ..) of k step kk at o[kk] + 4096 J
-//            (32 rows further keep the row's swizzle);
-//   MN mode: fragment J (columns r0 + 32 J ..) of k step kk: reads at
-//            o[J] + 8192 kk and o2[J] + 8192 kk (k-rows +16 keep the swizzle,
-//            k-rows +4 do not, hence two offsets).
+//   K mode : fragment J (rows r0 + kBlk J ..) of k step kk at
+//            o[kk] + 128 kBlk J (kBlk rows further keep the row's swizzle);
+//   MN mode: fragment J (columns r0 + kBlk J ..) of k step kk: reads at
+//            o[J] + 512 kKStep kk and o2[J] + 512 kKStep kk (k-rows +16 keep
+//            the swizzle, k-rows +4 do not, hence two offsets).
+constexpr int kMaxFrags = kMI > kNI ? kMI : kNI;
 struct FragOffs {
-  uint32_t o[4], o2[4];
+  uint32_t o[kMaxFrags > kKK ? kMaxFrags : kKK], o2[kMaxFrags];
 };
 
 template <bool MN>
 __device__ __forceinline__ FragOffs frag_offs(int r0, int lane) {
   FragOffs f;
   if constexpr (!MN) {
-    const int row = r0 + (lane & 31);
+    const int row = r0 + lane % kBlk;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f.o[kk] = 16u * (uint32_t)slot_k(row, 2 * kk + (lane >> 5));
-      f.o2[kk] = 0u;
-    }
+    for (int kk = 0; kk < kKK; ++kk) f.o[kk] = 16u * (uint32_t)slot_k(row, (kKStep / 8) * kk + lane / kBlk);
   } else {
+    // ds_read_b64_tr_b16 serves 16 lanes at a time: supplier lane 4j+q of a
+    // group points at k-row j, columns 4q..4q+3, and lane i of the group
+    // receives column i of those 4 k-rows.  Group g of the wave covers
+    // columns 16 (g % (kBlk/16)) .. +15 of the block and k-rows 8 (g / (kBlk/16)) + 0..3
+    // (first read) and + 4..7 (second read).
     const int g = lane >> 4, s = lane & 15;
-    const int krow = 8 * (g >> 1) + (s >> 2);
+    constexpr int kG = kBlk / 16;  // 16-lane groups across a block's columns: 2 or 1
+    const int krow = 8 * (g >> (kG - 1)) + (s >> 2);
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      const int col = r0 + 32 * J + 16 * (g & 1) + 4 * (s & 3);
+    for (int J = 0; J < kMaxFrags; ++J) {
+      const int col = r0 + kBlk * J + 16 * (g & (kG - 1)) + 4 * (s & 3);
       const int p = col >> 3, half = (col >> 2) & 1;
       f.o[J] = 16u * (uint32_t)slot_mn(krow, p) + 8u * half;
       f.o2[J] = 16u * (uint32_t)slot_mn(krow + 4, p) + 8u * half;
@@ -156,10 +179,10 @@ template <bool MN, int J>
 __device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, int kk) {
   const char* base = reinterpret_cast<const char*>(tile);
   if constexpr (!MN) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + f.o[kk] + 4096u * J));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + f.o[kk] + 128u * kBlk * J));
   } else {
-    const lds_bf16x4* p0 = (const lds_bf16x4*)(base + f.o[J] + 8192u * kk);
-    const lds_bf16x4* p1 = (const lds_bf16x4*)(base + f.o2[J] + 8192u * kk);
+    const lds_bf16x4* p0 = (const lds_bf16x4*)(base + f.o[J] + 512u * kKStep * kk);
+    const lds_bf16x4* p1 = (const lds_bf16x4*)(base + f.o2[J] + 512u * kKStep * kk);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p0));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p1));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -243,82 +266,100 @@ __device__ __forceinline__ RowsK rows_k(const uint16_t* base, int last, int ld) 
 }
 
 // ---- main loop -------------------------------------------------------------------
+// One accumulator block: kBlk x kBlk fp32, kBlk * kBlk / 64 values per lane.
+typedef float AccBlk __attribute__((ext_vector_type(kBlk * kBlk / 64)));
+
 struct Acc {
-  f32x16 c[kMI][kNI];
+  AccBlk c[kMI][kNI];
 };
 
+// Operand fragments in registers.  A block mi is used by the kNI MFMAs
+// (mi, 0 .. kNI-1) of a step, back to back, so the next step's A block mi is
+// read into the same registers right after the last of them.  Every B block
+// is used until the step's last row.  With four waves B fragments are
+// double-buffered by step parity (b[s & 1] for step s; a k-block has an
+// even number of steps) and the next step's are read over a step's first
+// half; with eight waves (fewer registers per wave) there is one B buffer
+// and block ni is re-read right after its last MFMA of the step (row
+// kMI - 1), kNI MFMAs before its next use, a lead the SIMD's other wave
+// stretches.
+constexpr bool kDoubleB = kWaves == 4;
 struct Frags {
-  bf16x8 a0, a1, a2, a3, b0, b1, b2, b3;  // a2, a3 unused with 8 waves
+  bf16x8 a[kMI], b[kDoubleB ? 2 : 1][kNI];
 };
+static_assert(!kDoubleB || kKK % 2 == 0, "B fragment buffers alternate by step parity");
 
-// Fragment J of a set (0..3: A blocks, 4..7: B blocks), by compile-time index.
-template <int J>
-__device__ __forceinline__ bf16x8& frag(Frags& f) {
-  static_assert(J >= 0 && J < 8, "fragment index");
-  if constexpr (J == 0) return f.a0;
-  else if constexpr (J == 1) return f.a1;
-  else if constexpr (J == 2) return f.a2;
-  else if constexpr (J == 3) return f.a3;
-  else if constexpr (J == 4) return f.b0;
-  else if constexpr (J == 5) return f.b1;
-  else if constexpr (J == 6) return f.b2;
-  else return f.b3;
-}
-template <int J>
-__device__ __forceinline__ const bf16x8& frag(const Frags& f) {
-  return frag<J>(const_cast<Frags&>(f));
-}
+// The B buffer that step parity p uses.
+__device__ __forceinline__ constexpr int bbuf(int p) { return kDoubleB ? p : 0; }
 
-// Fragment J of k step kk (J < 4: A block J, else B block J - 4) of the
-// k-block whose A and B tiles are at tA, tB in LDS.
-template <bool A_MN, bool B_MN, int J>
+// Fragment J (J < kMI: A block J, else B block J - kMI) of k step kk into
+// B buffer p.
+template <bool A_MN, bool B_MN, int J, int p>
 __device__ __forceinline__ void load_frag(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
-                                          int kk, Frags& g) {
-  if constexpr (J < 4) frag<J>(g) = frag_at<A_MN, J>(tA, fa, kk);
-  else frag<J>(g) = frag_at<B_MN, J - 4>(tB, fb, kk);
+                                          int kk, Frags& f) {
+  if constexpr (J < kMI) f.a[J] = frag_at<A_MN, J>(tA, fa, kk);
+  else f.b[bbuf(p)][J - kMI] = frag_at<B_MN, J - kMI>(tB, fb, kk);
 }
-
-// Fragment requested r-th (r < kReads) for a k step: A0, B0, B1, B2, B3, A1
-// (, A2, A3).  MFMA j of a step uses A (j >> 2) and B (j & 3), so with reads
-// completing in order the step's first MFMA waits for two reads only.
-__device__ __forceinline__ constexpr int read_frag(int r) { return r == 0 ? 0 : (r <= 4 ? r + 3 : r - 4); }
 
 // Row blocks: a wave may compute only its first kRB row blocks (kRB < kMI
 // when the tile's remaining rows are known to be padding); the fragments
-// and MFMAs of the others are skipped.  Fragment J (J < 4: A block J, else
-// B block J - 4) is needed iff this holds.
+// and MFMAs of the others are skipped.  Fragment J is needed iff this holds.
 template <int kRB>
-__device__ __forceinline__ constexpr bool frag_used(int J) { return J < 4 ? J < kRB : kRB > 0; }
+__device__ __forceinline__ constexpr bool frag_used(int J) { return J < kMI ? J < kRB : kRB > 0; }
 
-// Fragment J of k step kk if the wave uses it.
-template <bool A_MN, bool B_MN, int kRB, int J>
+template <bool A_MN, bool B_MN, int kRB, int J, int p>
 __device__ __forceinline__ void load_frag_if(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
-                                             int kk, Frags& g) {
-  if constexpr (frag_used<kRB>(J)) load_frag<A_MN, B_MN, J>(tA, tB, fa, fb, kk, g);
+                                             int kk, Frags& f) {
+  if constexpr (frag_used<kRB>(J)) load_frag<A_MN, B_MN, J, p>(tA, tB, fa, fb, kk, f);
 }
 
-template <bool A_MN, bool B_MN, int kRB = kMI>
+// All fragments of k step kk (B into buffer p): A0 and B0 first, so that
+// with reads completing in order the step's first MFMA waits for two only.
+template <bool A_MN, bool B_MN, int kRB, int p, int r = 0>
 __device__ __forceinline__ void load_frags(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
-                                           int kk, Frags& g) {
-  load_frag_if<A_MN, B_MN, kRB, read_frag(0)>(tA, tB, fa, fb, kk, g);
-  load_frag_if<A_MN, B_MN, kRB, read_frag(1)>(tA, tB, fa, fb, kk, g);
-  load_frag_if<A_MN, B_MN, kRB, read_frag(2)>(tA, tB, fa, fb, kk, g);
-  load_frag_if<A_MN, B_MN, kRB, read_frag(3)>(tA, tB, fa, fb, kk, g);
-  load_frag_if<A_MN, B_MN, kRB, read_frag(4)>(tA, tB, fa, fb, kk, g);
-  load_frag_if<A_MN, B_MN, kRB, read_frag(5)>(tA, tB, fa, fb, kk, g);
-  if constexpr (kReads == 8) {
-    load_frag_if<A_MN, B_MN, kRB, read_frag(6)>(tA, tB, fa, fb, kk, g);
-    load_frag_if<A_MN, B_MN, kRB, read_frag(7)>(tA, tB, fa, fb, kk, g);
+                                           int kk, Frags& f) {
+  if constexpr (r < kReads) {
+    constexpr int J = r == 0 ? 0 : (r <= kNI ? kMI + r - 1 : r - kNI);
+    load_frag_if<A_MN, B_MN, kRB, J, p>(tA, tB, fa, fb, kk, f);
+    load_frags<A_MN, B_MN, kRB, p, r + 1>(tA, tB, fa, fb, kk, f);
   }
 }
 
-// MFMA J of a k step: block (mi, ni) = (J >> 2, J & 3); skipped for row
-// blocks mi >= kRB.
-template <int J, int kRB = kMI>
+// B blocks r0 <= ni < r1 of k step kk into buffer p.
+template <bool A_MN, bool B_MN, int kRB, int p, int r0, int r1>
+__device__ __forceinline__ void load_bs(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
+                                        int kk, Frags& f) {
+  if constexpr (r0 < r1) {
+    load_frag_if<A_MN, B_MN, kRB, kMI + r0, p>(tA, tB, fa, fb, kk, f);
+    load_bs<A_MN, B_MN, kRB, p, r0 + 1, r1>(tA, tB, fa, fb, kk, f);
+  }
+}
+
+// A blocks r0 <= mi < r1 of k step kk.
+template <bool A_MN, bool B_MN, int kRB, int r0, int r1>
+__device__ __forceinline__ void load_as(const u32x4* tA, const u32x4* tB, const FragOffs& fa, const FragOffs& fb,
+                                        int kk, Frags& f) {
+  if constexpr (r0 < r1) {
+    load_frag_if<A_MN, B_MN, kRB, r0, 0>(tA, tB, fa, fb, kk, f);
+    load_as<A_MN, B_MN, kRB, r0 + 1, r1>(tA, tB, fa, fb, kk, f);
+  }
+}
+
+// MFMA J of a k step (B buffer p): block (mi, ni) = (J / kNI, J % kNI);
+// skipped for row blocks mi >= kRB.  The B fragment goes in as the X
+// operand and the A fragment as Y, so that lane l of block (mi, ni) holds
+// tile row kBlk mi + l % kBlk and, in elements 4q .. 4q+3, the four
+// consecutive columns kBlk ni + 4 kLPR q + 4 (l / kBlk) + 0..3.
+template <int J, int p, int kRB = kMI>
 __device__ __forceinline__ void mma1(const Frags& f, Acc& acc) {
-  constexpr int mi = J >> 2, ni = J & 3;
-  if constexpr (mi < kRB)
-    acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<4 + ni>(f), frag<mi>(f), acc.c[mi][ni], 0, 0, 0);
+  constexpr int mi = J / kNI, ni = J % kNI;
+  if constexpr (mi < kRB) {
+#if RLK_MFMA == 32
+    acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[bbuf(p)][ni], f.a[mi], acc.c[mi][ni], 0, 0, 0);
+#else
+    acc.c[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[bbuf(p)][ni], f.a[mi], acc.c[mi][ni], 0, 0, 0);
+#endif
+  }
 }
 
 // Wait until at most n (0 or kDma) of this thread's vector memory operations
@@ -343,66 +384,116 @@ static_assert(kDma == 8 || kDma == 4, "wait_vm counts assume 8 or 4 direct loads
 // builtin, which the compiler's own wait insertion takes into account).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// What a k step does besides its kMma MFMAs on f (16 with 4 waves, 8 with 8).
+// The schedule of a k-block.  Its kKK k steps of kMma MFMAs each (MFMA J
+// on row block J / kNI, column block J % kNI) prepare the next step: the B
+// fragments go into the other buffer, spread over the step's first half,
+// and each A fragment is re-read right after its last MFMA of the step.
+// The first kStepsB steps also issue the direct loads of the B tile of
+// block kt+2 (kDmaB), spread over the step.  The last step (kStepSwap) runs
+// half its MFMAs, waits until block kt+1 has landed and this wave's reads
+// are done, passes the block's one barrier, and then reads block kt+1's
+// first-step fragments (the A fragments whose MFMAs are done first, spread
+// with the B fragments over the second half) and issues the direct loads of
+// the A tile of block kt+2.
+constexpr int kStepsB = kKK > 2 ? kKK - 2 : 1;  // steps that carry the B-tile loads
+constexpr int kLoadsB = kDma / kStepsB;         // B-tile loads per such step
+constexpr int kHalf = kMma / 2;
+constexpr int kEarlyA = kHalf / kNI;            // A blocks done before the swap step's barrier
+static_assert(kDma % kStepsB == 0 && kMma % kLoadsB == 0, "B-tile loads spread evenly");
+static_assert(kHalf % kDma == 0 && kHalf % kNI == 0, "swap-step loads spread evenly");
+static_assert(kDoubleB || (kMI - 1) * kNI >= kHalf, "one B buffer: the last row runs after the swap step's barrier");
+
 enum StepKind {
-  kStepRead,   // request the next step's fragments (g: k step kk of tiles tA, tB): with 4 waves
-               // one per two MFMAs, with 8 one per MFMA from the first; with kDmaB also direct
-               // loads kDma/2 kB0 .. of a B tile (lb, k-block kb, wave slot base dB), one per
-               // four MFMAs
-  kStepSwap,   // last step of a k-block: kMma/2 MFMAs; wait until the next k-block has landed
-               // and this wave's reads are done; barrier; then the next block's first-step
-               // fragments (g from tA, tB: one per MFMA with 4 waves, two with 8) and one direct
-               // load of an A tile per MFMA (la, k-block kb, wave slot base dA)
+  kStepRead,   // next step's fragments (k step kk of tiles tA, tB); with kDmaB the B-tile loads
+               // kLoadsB kB0 .. of block kb into wave slot base dB
+  kStepSwap,   // last step of a k-block: the next block's first step from tA, tB (see above);
+               // A-tile loads of block kb into dA
   kStepLast,   // MFMAs only
 };
 
-// One k step.  No LDS wait is written for the fragment reads: before each
-// MFMA the compiler waits for exactly the reads it needs (LDS reads
-// complete in order).  In a kStepSwap step the barrier sits halfway: by
-// then every fragment of the block has long been read, so the wait before
-// it is short, and after it no wave reads the block's tiles.
-// Bare s_barrier: __syncthreads() would add a release fence that waits for
-// all outstanding loads.  Direct loads are spread one per one to four MFMAs
-// so that the address path never backs up into the wave's in-order issue.
-template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB = false, int kB0 = 0, int kRB = kMI, bool kLoadA = true,
-          class LA, class LB>
-__device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const u32x4* tA, const u32x4* tB,
-                                      const FragOffs& fa, const FragOffs& fb, int kk, const LA& la, const LB& lb,
-                                      int kb, uint32_t dA, uint32_t dB) {
-#define RLK_STEP(J)                                                                              \
-  if constexpr ((J) < kMma) {                                                                    \
-    constexpr int kHalf = kMma / 2;                                                              \
-    if constexpr (kKind == kStepRead && kReads == 8 && (J) % 2 == 0) {                           \
-      load_frag_if<A_MN, B_MN, kRB, read_frag((J) / 2)>(tA, tB, fa, fb, kk, g);                  \
-    } else if constexpr (kKind == kStepRead && kReads == 6 && (J) < 6) {                         \
-      load_frag_if<A_MN, B_MN, kRB, read_frag(J)>(tA, tB, fa, fb, kk, g);                        \
-    }                                                                                            \
-    if constexpr (kKind == kStepRead && kDmaB && (J) % 4 == 1) {                                 \
-      lb.one(kDma / 2 * kB0 + (J) / 4, kb, dB);                                                  \
-    } else if constexpr (kKind == kStepSwap && (J) == kHalf) {                                   \
-      wait_vm(kDma);                                                                             \
-      wait_lds();                                                                                \
-      __builtin_amdgcn_s_barrier();                                                              \
-      __builtin_amdgcn_sched_barrier(0);                                                         \
-    }                                                                                            \
-    if constexpr (kKind == kStepSwap && (J) >= kHalf) {                                          \
-      if constexpr (kReads == 8) {                                                               \
-        load_frag_if<A_MN, B_MN, kRB, read_frag((J) - kHalf)>(tA, tB, fa, fb, 0, g);             \
-      } else if constexpr (2 * ((J) - kHalf) < kReads) {                                         \
-        load_frag_if<A_MN, B_MN, kRB, read_frag(2 * ((J) - kHalf))>(tA, tB, fa, fb, 0, g);       \
-        load_frag_if<A_MN, B_MN, kRB, read_frag(2 * ((J) - kHalf) + 1)>(tA, tB, fa, fb, 0, g);   \
-      }                                                                                          \
-      if constexpr (kLoadA) la.one((J) - kHalf, kb, dA);                                         \
-    }                                                                                            \
-    mma1<J, kRB>(f, acc);                                                                        \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
+// First of m items spread evenly over a span of n MFMAs that is due at
+// MFMA j of the span.
+__device__ __forceinline__ constexpr int spread(int j, int n, int m) { return (j * m + n - 1) / n; }
+
+// MFMA J of a k step (B buffer p) with what comes before and after it.  No
+// LDS wait is written for the fragment reads: before each MFMA the compiler
+// waits for exactly the reads it needs (LDS reads complete in order).  The
+// swap step's barrier is a bare s_barrier: __syncthreads() would add a
+// release fence that waits for all outstanding loads.
+template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB, int kB0, int kRB, bool kLoadA, int p, int J, class LA,
+          class LB>
+__device__ __forceinline__ void kslot(Frags& f, Acc& acc, const u32x4* tA, const u32x4* tB, const FragOffs& fa,
+                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, uint32_t dA,
+                                      uint32_t dB) {
+  constexpr int mi = J / kNI, ni = J % kNI;
+  if constexpr (kKind == kStepRead) {
+    if constexpr (kDoubleB && J < kHalf)
+      load_bs<A_MN, B_MN, kRB, p ^ 1, spread(J, kHalf, kNI), spread(J + 1, kHalf, kNI)>(tA, tB, fa, fb, kk, f);
+    if constexpr (kDmaB && J % (kMma / kLoadsB) == 1 % (kMma / kLoadsB))
+      lb.one(kLoadsB * kB0 + J / (kMma / kLoadsB), kb, dB);
+  } else if constexpr (kKind == kStepSwap && J >= kHalf) {
+    if constexpr (J == kHalf) {
+      wait_vm(kDma);
+      wait_lds();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int j = J - kHalf;
+    load_as<A_MN, B_MN, kRB, spread(j, kHalf, kEarlyA), spread(j + 1, kHalf, kEarlyA)>(tA, tB, fa, fb, 0, f);
+    if constexpr (kDoubleB)
+      load_bs<A_MN, B_MN, kRB, p ^ 1, spread(j, kHalf, kNI), spread(j + 1, kHalf, kNI)>(tA, tB, fa, fb, 0, f);
+    if constexpr (kLoadA && j % (kHalf / kDma) == 0) la.one(j / (kHalf / kDma), kb, dA);
   }
-  static_assert(kDma == kMma / 2, "one direct load per MFMA in the second half of a swap step");
-  static_assert(kDma == 2 * (kMma / 4), "the B tile's loads spread over two read steps");
+  mma1<J, p, kRB>(f, acc);
+  if constexpr (!kDoubleB && mi == kMI - 1) {
+    // B block ni is done for this step (one B buffer): the next step's
+    // (in the swap step, the next block's first step, after the barrier)
+    if constexpr (kKind == kStepRead) load_bs<A_MN, B_MN, kRB, 0, ni, ni + 1>(tA, tB, fa, fb, kk, f);
+    else if constexpr (kKind == kStepSwap) load_bs<A_MN, B_MN, kRB, 0, ni, ni + 1>(tA, tB, fa, fb, 0, f);
+  }
+  if constexpr (ni == kNI - 1) {
+    // A block mi is done for this step
+    if constexpr (kKind == kStepRead) load_as<A_MN, B_MN, kRB, mi, mi + 1>(tA, tB, fa, fb, kk, f);
+    else if constexpr (kKind == kStepSwap && mi >= kEarlyA) load_as<A_MN, B_MN, kRB, mi, mi + 1>(tA, tB, fa, fb, 0, f);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  RLK_STEP(0) RLK_STEP(1) RLK_STEP(2) RLK_STEP(3) RLK_STEP(4) RLK_STEP(5) RLK_STEP(6) RLK_STEP(7)
-  RLK_STEP(8) RLK_STEP(9) RLK_STEP(10) RLK_STEP(11) RLK_STEP(12) RLK_STEP(13) RLK_STEP(14) RLK_STEP(15)
-#undef RLK_STEP
+}
+
+template <bool A_MN, bool B_MN, StepKind kKind, bool kDmaB, int kB0, int kRB, bool kLoadA, int p, class LA, class LB,
+          int... Js>
+__device__ __forceinline__ void kslots(std::integer_sequence<int, Js...>, Frags& f, Acc& acc, const u32x4* tA,
+                                       const u32x4* tB, const FragOffs& fa, const FragOffs& fb, int kk, const LA& la,
+                                       const LB& lb, int kb, uint32_t dA, uint32_t dB) {
+  (kslot<A_MN, B_MN, kKind, kDmaB, kB0, kRB, kLoadA, p, Js>(f, acc, tA, tB, fa, fb, kk, la, lb, kb, dA, dB), ...);
+}
+
+// One k step with B buffer p: kMma MFMAs, plus (by kKind) the next step's
+// fragments (k step kk of tA, tB) and direct loads.
+template <bool A_MN, bool B_MN, StepKind kKind, int p, bool kDmaB = false, int kB0 = 0, int kRB = kMI,
+          bool kLoadA = true, class LA, class LB>
+__device__ __forceinline__ void kstep(Frags& f, Acc& acc, const u32x4* tA, const u32x4* tB, const FragOffs& fa,
+                                      const FragOffs& fb, int kk, const LA& la, const LB& lb, int kb, uint32_t dA,
+                                      uint32_t dB) {
+  __builtin_amdgcn_sched_barrier(0);
+  kslots<A_MN, B_MN, kKind, kDmaB, kB0, kRB, kLoadA, p>(std::make_integer_sequence<int, kMma>{}, f, acc, tA, tB, fa,
+                                                        fb, kk, la, lb, kb, dA, dB);
+}
+
+// The read steps kS .. kKK-2 of a k-block (step s reads step s + 1's
+// fragments; steps below kStepsB issue the B-tile loads of block kb when
+// `loads`).
+template <bool A_MN, bool B_MN, int kRB, bool kLoadA, int kS, class LA, class LB>
+__device__ __forceinline__ void read_steps(Frags& f, Acc& acc, const u32x4* tA, const u32x4* tB, const FragOffs& fa,
+                                           const FragOffs& fb, const LA& la, const LB& lb, int kb, uint32_t dB,
+                                           bool loads) {
+  if constexpr (kS < kKK - 1) {
+    if (loads)
+      kstep<A_MN, B_MN, kStepRead, kS & 1, (kS < kStepsB), kS, kRB, kLoadA>(f, acc, tA, tB, fa, fb, kS + 1, la, lb,
+                                                                           kb, 0u, dB);
+    else
+      kstep<A_MN, B_MN, kStepRead, kS & 1, false, kS, kRB, kLoadA>(f, acc, tA, tB, fa, fb, kS + 1, la, lb, 0, 0u, 0u);
+    read_steps<A_MN, B_MN, kRB, kLoadA, kS + 1>(f, acc, tA, tB, fa, fb, la, lb, kb, dB, loads);
+  }
 }
 
 // nk k-blocks of kBK.  LA / LB: loaders with one(i, kt, m0w) / dma(kt, m0w)
@@ -410,12 +501,7 @@ __device__ __forceinline__ void kstep(const Frags& f, Frags& g, Acc& acc, const 
 // kLdsU4 words = a ring of 5 operand-tile slots.  Tile q = 2 kt (B of block
 // kt) or 2 kt + 1 (A of block kt) lives in slot q mod 5, so at any time the
 // ring holds the two tiles being read, the next block's two and one more.
-// Per k-block kt, four MFMA k steps of 16 MFMAs each, each requesting the
-// next step's fragments:
-//   step 0 | step 1     (with the loads of B of block kt+2, 1 per 4 MFMAs)
-//   step 2 | step 3: 8 MFMAs, wait for block kt+1, barrier, 8 MFMAs with
-//   the reads of block kt+1's step 0 and the loads of A of block kt+2
-// so B tiles are issued about 1.5 blocks and A tiles 1 block before use.
+// B tiles are issued about 1.5 blocks and A tiles 1 block before use.
 // Loads past the last block repeat the last block's tile into the free slot
 // (uniform load counts; nothing reads that copy); all have landed on return.
 //
@@ -441,7 +527,7 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
                                         const Tail& tail = Tail{}) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ra0 = kWaveRows * wave_m(w), rb0 = 128 * wave_n(w);
-  static_assert(kKK == 4 && kSlots == 5, "schedule written for four k steps and five tile slots");
+  static_assert(kSlots == 5, "schedule written for five tile slots");
   // direct-load slot base of this wave in slot 0; slot s is kTileB * s further
   const uint32_t m0s = dma_wave_base(lds_addr(lds));
   constexpr uint32_t kTileB = 16u * kTileU4;
@@ -456,9 +542,9 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
   else wait_vm(kDma);
   __builtin_amdgcn_s_barrier();
   const FragOffs fa = frag_offs<A_MN>(ra0, lane), fb = frag_offs<B_MN>(rb0, lane);
-  Frags f, g;
+  Frags f;
   int sb = 0;  // slot of B of the current block (A is in slot sb + 1 mod 5)
-  load_frags<A_MN, B_MN, kRB>(lds + kTileU4, lds, fa, fb, 0, f);
+  load_frags<A_MN, B_MN, kRB, 0>(lds + kTileU4, lds, fa, fb, 0, f);
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int sa = sb == 4 ? 0 : sb + 1;
     const u32x4* tA = lds + sa * kTileU4;
@@ -467,19 +553,12 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
     // slot sb (freed by B of block kt at this block's barrier)
     const int k2 = min(kt + 2, nk - 1);
     const int sb2 = sb == 0 ? 4 : sb - 1;
-    kstep<A_MN, B_MN, kStepRead, true, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 1, la, lb, k2, 0u,
-                                                         m0s + sb2 * kTileB);
-    f = g;
-    kstep<A_MN, B_MN, kStepRead, true, 1, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 2, la, lb, k2, 0u,
-                                                         m0s + sb2 * kTileB);
-    f = g;
-    kstep<A_MN, B_MN, kStepRead, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 3, la, lb, 0, 0u, 0u);
-    f = g;
+    read_steps<A_MN, B_MN, kRB, kLoadA, 0>(f, acc, tA, tB, fa, fb, la, lb, k2, m0s + sb2 * kTileB, true);
     const int sbn = sb >= 3 ? sb - 3 : sb + 2;  // slot of B of block kt+1
     const int san = sbn == 4 ? 0 : sbn + 1;
-    kstep<A_MN, B_MN, kStepSwap, false, 0, kRB, kLoadA>(f, g, acc, lds + san * kTileU4, lds + sbn * kTileU4, fa, fb,
-                                                        0, la, lb, k2, m0s + sb * kTileB, 0u);
-    f = g;
+    kstep<A_MN, B_MN, kStepSwap, (kKK - 1) & 1, false, 0, kRB, kLoadA>(f, acc, lds + san * kTileU4,
+                                                                     lds + sbn * kTileU4, fa, fb, 0, la, lb, k2,
+                                                                     m0s + sb * kTileB, 0u);
     sb = sbn;
   }
   {
@@ -487,12 +566,8 @@ __device__ __forceinline__ void gemm256(const LA& la, const LB& lb, int nk, Acc&
     const int sa = sb == 4 ? 0 : sb + 1;
     const u32x4* tA = lds + sa * kTileU4;
     const u32x4* tB = lds + sb * kTileU4;
-#pragma unroll
-    for (int kk = 0; kk < kKK - 1; ++kk) {
-      kstep<A_MN, B_MN, kStepRead, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, kk + 1, la, lb, 0, 0u, 0u);
-      f = g;
-    }
-    kstep<A_MN, B_MN, kStepLast, false, 0, kRB, kLoadA>(f, g, acc, tA, tB, fa, fb, 0, la, lb, 0, 0u, 0u);
+    read_steps<A_MN, B_MN, kRB, kLoadA, 0>(f, acc, tA, tB, fa, fb, la, lb, 0, 0u, false);
+    kstep<A_MN, B_MN, kStepLast, (kKK - 1) & 1, false, 0, kRB, kLoadA>(f, acc, tA, tB, fa, fb, 0, la, lb, 0, 0u, 0u);
   }
   // every load issued has landed and every wave is done with the ring
   wait_vm(0);
@@ -503,16 +578,21 @@ __device__ __forceinline__ void acc_zero(Acc& acc) {
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) acc.c[mi][ni] = f32x16{};
+    for (int ni = 0; ni < kNI; ++ni) acc.c[mi][ni] = AccBlk{};
 }
 
 // Tile-local row held by lane l in block mi of wave (wm, *).
-__device__ __forceinline__ int acc_row(int wm, int mi, int lane) { return kWaveRows * wm + 32 * mi + (lane & 31); }
+__device__ __forceinline__ int acc_row(int wm, int mi, int lane) {
+  return kWaveRows * wm + kBlk * mi + lane % kBlk;
+}
 
-// Tile-local column of elements 4g .. 4g+3 (first of four) of block ni for
-// lane l in wave (*, wn).
-__device__ __forceinline__ int acc_col4(int wn, int ni, int g, int lane) {
-  return 128 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
+// Which of the kLPR lanes holding a row lane l is (0 .. kLPR-1).
+__device__ __forceinline__ int row_lane(int lane) { return lane / kBlk; }
+
+// Tile-local column of elements 4q .. 4q+3 (first of four consecutive
+// columns; q < kQL) of block ni for lane l in wave (*, wn).
+__device__ __forceinline__ int acc_col4(int wn, int ni, int q, int lane) {
+  return 128 * wn + kBlk * ni + 4 * kLPR * q + 4 * row_lane(lane);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own

@@ -120,36 +120,6 @@ __device__ __forceinline__ void chunk_cols(const SplitGeom& gm, int g, int& c0, 
   c1 = min(c0 + kChunk, send);
 }
 
-// sum over k in [k0, k0 + N) of e(v[k] - m) as a balanced pairwise tree
-// (adjacent pairs, then pairs of pairs): the same additions as tree_sum64
-// on those values, evaluated subtree by subtree so that only one partial
-// sum per level is live.
-template <int N>
-__device__ __forceinline__ float exp_tree(const float (&v)[64], int k0, float m) {
-  if constexpr (N == 1) {
-    return rlk_exp(v[k0] - m);
-  } else {
-    const float l = exp_tree<N / 2>(v, k0, m);
-    const float r = exp_tree<N / 2>(v, k0 + N / 2, m);
-    return l + r;
-  }
-}
-
-// Balanced pairwise tree over e[0..63]: adjacent pairs, then pairs of pairs.
-// (Fixed-size levels: every index is a compile-time constant.)
-__device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
-  float t32[32], t16[16], t8[8], t4[4];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) t32[k] = e[2 * k] + e[2 * k + 1];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) t16[k] = t32[2 * k] + t32[2 * k + 1];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) t8[k] = t16[2 * k] + t16[2 * k + 1];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) t4[k] = t8[2 * k] + t8[2 * k + 1];
-  return (t4[0] + t4[1]) + (t4[2] + t4[3]);
-}
-
 // ---------------------------------------------------------------------------
 // Forward chunk statistics on 256 x 256 tiles.
 //
@@ -159,47 +129,100 @@ __device__ __forceinline__ float tree_sum64(const float (&e)[64]) {
 // (g = local split * cps + chunk) for active row i, and zt[i] = the target's
 // logit, written by the one chunk that holds it.
 //
-// A row's 128 chunk columns sit in one lane pair: the lane of half h
-// (h = 0, 1) holds the 64 columns c with (c >> 2) & 1 == h, in ascending
-// order as its elements k = 16 ni + r (column 32 ni + 8 (r >> 2) + 4 h + (r & 3)).
-// Chunk statistics of one row over the chunk's valid columns:
+// A row's 128 chunk columns sit in kLPR lanes (the MFMA output layout):
+// lane part r = row_lane(l) (0 .. kLPR-1) holds the kRowVals columns c with
+// (c >> 2) % kLPR == r, in ascending order as its elements
+// k = 4 kQL ni + 4 q + u, column chunk_col(k) + 4 r.  Chunk statistics of
+// one row over the chunk's valid columns:
 //   m   = max_c z_c (exact; invalid columns enter as -inf);
 //   e_c = exp(z_c - m) (0 for invalid columns);
-//   s   = T(e of half 0) + T(e of half 1), T = balanced pairwise tree over
-//         the half's 64 columns in ascending order.
+//   s   = combination over the parts of T(e of part r), T = balanced
+//         pairwise tree over the part's columns in ascending order; two
+//         parts (32 x 32 MFMAs): T0 + T1; four (16 x 16): (T0 + T1) + (T2 + T3).
 // ---------------------------------------------------------------------------
-// (m, s) of one row of a chunk from this lane's 64 values v and its
-// partner lane's (the other half of the row); columns outside the chunk
-// enter as -inf (they do not move the max, and their e is exp(-inf) = 0).
-__device__ __forceinline__ float2 chunk_stats(const float (&v)[64]) {
+constexpr int kRowVals = kNI * kQL * 4;  // a lane's values of one row of a chunk: 64 or 32
+// Row blocks whose per-row inputs a tile kernel loads under the last k-block
+// (the rest after the engine returns): all with four waves, one with eight.
+constexpr int kTailRows = kWaves == 8 ? 1 : kMI;
+
+// Chunk column of a lane's value k, relative to 4 row_lane(l).
+__device__ __forceinline__ constexpr int chunk_col(int k) {
+  return kBlk * (k / (4 * kQL)) + 4 * kLPR * (k / 4 % kQL) + (k & 3);
+}
+
+// The lane value index of chunk column c (in the lane with row_lane == (c >> 2) % kLPR).
+__device__ __forceinline__ int chunk_val(int c) { return 4 * kQL * (c / kBlk) + 4 * (c % kBlk / (4 * kLPR)) + (c & 3); }
+
+// Max and sum of one row over the kLPR lanes that hold it, the same value in
+// each of them: with two parts the lane pair (l, l ^ 32); with four the
+// lanes l ^ 16, then l ^ 32, so the sum is (s0 + s1) + (s2 + s3) for the
+// parts' partials in part order (fp32 addition is commutative, so every
+// lane forms the same sums).
+__device__ __forceinline__ float row_max(float x) {
+  if constexpr (kLPR == 2) {
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return fmaxf(lo, hi);
+  } else {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+  }
+}
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (kLPR == 2) {
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return lo + hi;
+  } else {
+    x = x + __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  }
+}
+
+// sum over k in [k0, k0 + N) of e(v[k] - m) as a balanced pairwise tree
+// (adjacent pairs, then pairs of pairs), evaluated subtree by subtree so
+// that only one partial sum per level is live.
+template <int N>
+__device__ __forceinline__ float exp_tree(const float (&v)[kRowVals], int k0, float m) {
+  if constexpr (N == 1) {
+    return rlk_exp(v[k0] - m);
+  } else {
+    const float l = exp_tree<N / 2>(v, k0, m);
+    const float r = exp_tree<N / 2>(v, k0 + N / 2, m);
+    return l + r;
+  }
+}
+
+// (m, s) of one row of a chunk from this lane's values v and those of the
+// other lanes of the row; columns outside the chunk enter as -inf (they do
+// not move the max, and their e is exp(-inf) = 0).
+__device__ __forceinline__ float2 chunk_stats(const float (&v)[kRowVals]) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < 64; ++k) mx = fmaxf(mx, v[k]);
-  float lo, hi;
-  lane_halves(mx, lo, hi);
-  mx = fmaxf(lo, hi);
-  lane_halves(exp_tree<64>(v, 0, mx), lo, hi);
-  return make_float2(mx, lo + hi);
+  for (int k = 0; k < kRowVals; ++k) mx = fmaxf(mx, v[k]);
+  mx = row_max(mx);
+  return make_float2(mx, row_sum(exp_tree<kRowVals>(v, 0, mx)));
 }
 
 // Engine call for a K-mode x K-mode tile.  kSkinny = 1..3 (four-wave
 // layout only): the caller guarantees that every valid row of the tile lies
 // below 32 kSkinny (a batch of at most 96 rows, one row tile), so the
 // waves holding rows 128..255 compute nothing, the others only their first
-// kSkinny row blocks, and only the waves whose load rows (64 w .. 64 w + 63)
-// meet those rows load the A tile.  Every element that is computed is the
-// same MFMA chain as in the full tile.
+// 32 kSkinny rows (kRB row blocks), and only the waves whose load rows
+// (64 w .. 64 w + 63) meet those rows load the A tile.  Every element that
+// is computed is the same MFMA chain as in the full tile.
 template <int kSkinny, class LA, class LB, class Tail>
 __device__ __forceinline__ void gemm_kk(const LA& la, const LB& lb, int nk, Acc& acc, u32x4* lds, const Tail& tail) {
   if constexpr (kSkinny == 0 || kWaves != 4) {
     gemm256<false, false>(la, lb, nk, acc, lds, tail);
   } else {
-    static_assert(kSkinny >= 1 && kSkinny < kMI, "row blocks of the first wave row");
+    constexpr int kRB = kSkinny * 32 / kBlk;  // row blocks below 32 kSkinny
+    static_assert(kSkinny >= 1 && kRB < kMI, "row blocks of the first wave row");
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w == 0) {
-      gemm256<false, false, kSkinny, true>(la, lb, nk, acc, lds, tail);
+      gemm256<false, false, kRB, true>(la, lb, nk, acc, lds, tail);
     } else if (w == 2) {
-      gemm256<false, false, kSkinny, false>(la, lb, nk, acc, lds, tail);
+      gemm256<false, false, kRB, false>(la, lb, nk, acc, lds, tail);
     } else if (w == 1 && kSkinny >= 3) {
       gemm256<false, false, 0, true>(la, lb, nk, acc, lds, tail);
     } else {
@@ -231,18 +254,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   if (c0 >= send) return;
   const int c1 = min(c0 + kBN, send);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w), hh = lane >> 5;
-  // targets (and, kSave, original rows) of this lane's rows: loaded while
-  // the last k-block's MFMAs run, so that nothing of them is kept through
-  // the main loop
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave_m(w),
+            wn = wave_n(w);
+  // targets (and, kSave, original rows) of this lane's rows: those of the
+  // first kTailRows row blocks are loaded while the last k-block's MFMAs run
+  // (so that nothing of them is kept through the main loop), the others when
+  // the epilogue starts, landing while the first blocks are processed (with
+  // eight waves the last k-block leaves registers for one block's only)
   int tgt[kMI], trow[kMI];
+  const auto load_row = [&](int mi, int ln) {
+    const int r = min(i0 + acc_row(wm, mi, ln), n_act - 1);
+    tgt[mi] = a.yA[r];
+    if (kSave) trow[mi] = a.idx[r];
+  };
   const auto load_rows = [&]() {
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      const int r = min(i0 + acc_row(wm, mi, lane), n_act - 1);
-      tgt[mi] = a.yA[r];
-      if (kSave) trow[mi] = a.idx[r];
-    }
+    for (int mi = 0; mi < kTailRows; ++mi) load_row(mi, lane);
   };
 
   const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
@@ -255,64 +282,65 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   const int width = min(cc0 + kChunk, c1) - cc0;
   if (width <= 0) return;
   const int g = sl * a.gm.cps + 2 * j + wn;
-  const int lim = width - 4 * hh;  // element (ni, r) is valid iff 32 ni + 8 (r >> 2) + (r & 3) < lim
+  // the lane's indices again, from an opaque copy of the lane id: computed
+  // before the main loop they would be kept live through it
+  int le = lane;
+  asm volatile("" : "+v"(le));
+  const int rl = row_lane(le);
+  const int lim = width - 4 * rl;  // value k is valid iff chunk_col(k) < lim
+#pragma unroll
+  for (int mi = kTailRows; mi < kMI; ++mi) load_row(mi, le);
 
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
-    const int i = i0 + acc_row(wm, mi, lane);
-    // the row's 64 values of this lane, out of the accumulator once
-    // one row block at a time: its values leave the accumulators here and
-    // not earlier (the scheduler would otherwise hoist every block's moves)
+    const int i = i0 + acc_row(wm, mi, le);
+    // the row's values of this lane, out of the accumulator once, one row
+    // block at a time: its values leave the accumulators here and not
+    // earlier (the scheduler would otherwise hoist every block's moves)
     __builtin_amdgcn_sched_barrier(0);
-    float v[64];
+    float v[kRowVals];
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[16 * ni + r] = acc.c[mi][ni][r];
+      for (int r = 0; r < 4 * kQL; ++r) v[4 * kQL * ni + r] = acc.c[mi][ni][r];
     if (kSave && i < n_act) {
-      // columns cc0 + 32 ni + 8 q + 4 hh + 0..3 (the chunk's first `width`);
+      // columns cc0 + 4 rl + chunk_col(k) (the chunk's first `width`);
       // cc0 - sbeg is a multiple of 128, so every float4 is 16-byte aligned
-      float* zr = a.zsave + (size_t)trow[mi] * a.ldzs + (size_t)(a.gm.s0 + sl) * a.zs_spad + (cc0 - sbeg) + 4 * hh;
+      float* zr = a.zsave + (size_t)trow[mi] * a.ldzs + (size_t)(a.gm.s0 + sl) * a.zs_spad + (cc0 - sbeg) + 4 * rl;
       if (width == kChunk) {
         // a whole chunk (wave-uniform): every float4 is inside it
 #pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float* e = v + 16 * ni + 4 * q;
-            *reinterpret_cast<float4*>(zr + 32 * ni + 8 * q) = make_float4(e[0], e[1], e[2], e[3]);
-          }
+        for (int k = 0; k < kRowVals; k += 4)
+          *reinterpret_cast<float4*>(zr + chunk_col(k)) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
       } else {
 #pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
+        for (int k = 0; k < kRowVals; k += 4) {
+          const int c = chunk_col(k);  // column of element k, relative to cc0 + 4 rl
+          if (c + 4 <= lim) {
+            *reinterpret_cast<float4*>(zr + c) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+          } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = 32 * ni + 8 * q;  // column of element 0, relative to cc0 + 4 hh
-            const float* e = v + 16 * ni + 4 * q;
-            if (c + 4 <= lim) {
-              *reinterpret_cast<float4*>(zr + c) = make_float4(e[0], e[1], e[2], e[3]);
-            } else {
-#pragma unroll
-              for (int u = 0; u < 4; ++u)
-                if (c + u < lim) zr[c + u] = e[u];
-            }
+            for (int u = 0; u < 4; ++u)
+              if (c + u < lim) zr[c + u] = v[k + u];
           }
+        }
       }
     }
     // target logit: rare (a row's target lies in a given chunk about once in
     // a thousand).  When some lane of the wave needs one, the wave's values
     // go through LDS, which is free once the engine has returned: lane l
     // writes its element k at float4 slot 64 (k >> 2) + l of the wave's
-    // 16 KB and reads back only its own slots.
+    // 16 kRowVals float4 slots and reads back only its own.
     const int tc = tgt[mi] - cc0;
-    const bool hit = i < n_act && tc >= 0 && tc < width && ((tc >> 2) & 1) == hh;
+    const bool hit = i < n_act && tc >= 0 && tc < width && ((tc >> 2) & (kLPR - 1)) == rl;
     if (__builtin_amdgcn_ballot_w64(hit)) {
-      float4* sl = reinterpret_cast<float4*>(lds) + 1024 * w;
+      float4* sl = reinterpret_cast<float4*>(lds) + 16 * kRowVals * w;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) sl[64 * q + lane] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      for (int q = 0; q < kRowVals / 4; ++q)
+        sl[64 * q + le] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       if (hit) {
-        const int k = ((tc >> 5) << 4) | (((tc >> 3) & 3) << 2) | (tc & 3);
-        a.zt[i] = reinterpret_cast<const float*>(sl + 64 * (k >> 2) + lane)[k & 3];
+        const int k = chunk_val(tc);
+        a.zt[i] = reinterpret_cast<const float*>(sl + 64 * (k >> 2) + le)[k & 3];
       }
     }
     // the short last chunk of a split (a wave-uniform branch): its missing
@@ -320,13 +348,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
     // not used after the statistics)
     if (width < kChunk) {
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * ni + 8 * (r >> 2) + (r & 3) >= lim) v[16 * ni + r] = -INFINITY;
+      for (int k = 0; k < kRowVals; ++k)
+        if (chunk_col(k) >= lim) v[k] = -INFINITY;
     }
     const float2 st = chunk_stats(v);
-    if (hh == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = st;
+    if (rl == 0 && i < n_act) a.rec[(size_t)g * a.rec_stride + i] = st;
   }
 }
 
@@ -492,10 +518,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   const int valid_s = max(0, min(a.gm.S, a.gm.V - sbeg));  // columns of this split
   const int c0 = sbeg + j * kBN;
   const int c1 = sbeg + min(j * kBN + kBN, valid_s);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
-  float4 ri[kMI];  // this lane's rows, loaded ahead of the main loop
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave_m(w),
+            wn = wave_n(w);
+  // this lane's rows' {lse, g, target}: those of the first kTailRows row
+  // blocks loaded under the last k-block, the others when the epilogue
+  // starts (as in fwd_tiles)
+  float4 ri[kMI];
+  const auto load_rows = [&]() {
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, lane)];
+    for (int mi = 0; mi < kTailRows; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, lane)];
+  };
   Acc acc;
   acc_zero(acc);
   {
@@ -503,8 +535,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
     // runs, on W's first row; its columns are all written as zeros below
     const RowsK A = rows_k(a.hA + (size_t)i0 * a.H, kBM - 1, a.H);
     const RowsK B = c0 < c1 ? rows_k(a.W + (size_t)c0 * a.H, c1 - 1 - c0, a.H) : rows_k(a.W, 0, a.H);
-    gemm256<false, false>(A, B, a.H / kBK, acc, lds);
+    gemm256<false, false>(A, B, a.H / kBK, acc, lds, load_rows);
   }
+  // the lane's indices again, from an opaque copy of the lane id (see fwd_tiles)
+  int le = lane;
+  asm volatile("" : "+v"(le));
+#pragma unroll
+  for (int mi = kTailRows; mi < kMI; ++mi) ri[mi] = a.rowinfo[i0 + acc_row(wm, mi, le)];
   uint16_t* dzs = a.dZ + (size_t)sc * a.bg.S_pad;
   // The dz values go through LDS (free after the main loop) so that every
   // global store writes whole rows.  LDS tile: 256 rows x 512 bytes; the
@@ -522,21 +559,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   const bool full = i0 + kWaveRows * wm + kWaveRows <= n_act && wc0 + 128 <= valid_s;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
-    const int r = acc_row(wm, mi, lane);
+    const int r = acc_row(wm, mi, le);
     const bool rvalid = i0 + r < n_act;
     const float L = ri[mi].x, gi = ri[mi].y;
     const int yl = __float_as_int(ri[mi].z) - sbeg;  // target column within the split
     // does this lane hold its row's target column?  (rare)
     const int tl = yl - wc0;
-    const bool hit = tl >= 0 && tl < 128 && ((tl >> 2) & 1) == (lane >> 5);
+    const bool hit = tl >= 0 && tl < 128 && ((tl >> 2) & (kLPR - 1)) == row_lane(le);
     if (full && !__builtin_amdgcn_ballot_w64(hit)) {
       // every element is off-target, active and inside the split: the same
       // formula with delta = 0, without the per-element tests
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = acc_col4(wn, ni, q, lane);
+        for (int q = 0; q < kQL; ++q) {
+          const int c = acc_col4(wn, ni, q, le);
           float d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) d[e] = gi * (0.f - rlk_exp(acc.c[mi][ni][4 * q + e] - L));
@@ -546,9 +583,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (j * kBN + 128 * wn + 32 * ni + 8 * q >= a.bg.S_pad) continue;  // wave-uniform; never stored
-          const int c = acc_col4(wn, ni, q, lane);
+        for (int q = 0; q < kQL; ++q) {
+          // wave-uniform: the group's columns start at 128 wn + kBlk ni + 4 kLPR q
+          if (j * kBN + 128 * wn + kBlk * ni + 4 * kLPR * q >= a.bg.S_pad) continue;  // never stored
+          const int c = acc_col4(wn, ni, q, le);
           const int vl0 = j * kBN + c;
           float d[4];
 #pragma unroll
@@ -567,12 +605,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
   // lane l the 16-byte unit l & 31 of row 2 it + (l >> 5); units past the
   // split's padded width belong to the next split and are not written
   constexpr int kRowsW = kBM / kWaves;
-  const int u = lane & 31;
+  const int u = le & 31;
   const int col = j * kBN + 8 * u;  // column within the split
   if (col < a.bg.S_pad) {
 #pragma unroll
     for (int it = 0; it < kRowsW / 2; ++it) {
-      const int r = kRowsW * w + 2 * it + (lane >> 5);
+      const int r = kRowsW * w + 2 * it + (le >> 5);
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 512u * r + 16u * (u ^ (r & 31)));
       // streaming store: dz is read back only by the next launch, so it
       // should not displace the W and h lines the other tiles still use
@@ -714,9 +752,9 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (n0 + 128 * wn + 32 * ni + 8 * q >= a.H) continue;  // wave-uniform
-        const f32x16& c = acc.c[mi][ni];
+      for (int q = 0; q < kQL; ++q) {
+        if (n0 + 128 * wn + kBlk * ni + 4 * kLPR * q >= a.H) continue;  // wave-uniform
+        const AccBlk& c = acc.c[mi][ni];
         *reinterpret_cast<float4*>(out + (size_t)v * a.H + n0 + acc_col4(wn, ni, q, lane)) =
             make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
       }
@@ -730,10 +768,10 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
 // kFirst / kLast: the group is the first / last one (compile-time, so that
 // the accumulators never merge across a branch).  Tile id: (row tile, H tile).
 //
-// kPart: the tile's rows in two passes, id = 2 tile + p.  Pass p reads the
-// dz tile from 16 kMI p rows further down and every wave computes only its
-// first kMI / 2 row blocks, i.e. tile rows 16 kMI p + kWaveRows wm + 0 ..
-// 16 kMI - 1 (the two passes cover all of them); only the waves whose load
+// kPart: the tile's rows in two passes, id = 2 tile + p.  With R = kWaveRows
+// / 2 rows per pass, pass p reads the dz tile from R p rows further down and
+// every wave computes only its first kMI / 2 row blocks, i.e. tile rows
+// R p + kWaveRows wm + 0 .. R - 1 (the two passes cover all of them); only the waves whose load
 // rows meet those rows load the dz tile.  Twice the workgroups, each with
 // half the MFMAs per k-block and three quarters of the loads: the k-block
 // is then bound by its loads at ~70 % of a whole tile's time.  For
@@ -747,13 +785,8 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
   const int pass = id % kPasses;
   int rt, nt;
   grouped_tile(id / kPasses, rtiles, rt, nt, a.n_tiles, row_group(rtiles));
-  const int i0 = rt * kBM + 32 * kBlocks * pass, n0 = nt * kBN;
+  const int i0 = rt * kBM + kBlk * kBlocks * pass, n0 = nt * kBN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);
-  int dst[kMI];  // output rows of this lane's active rows, loaded ahead
-  if (kLast) {
-#pragma unroll
-    for (int mi = 0; mi < kBlocks; ++mi) dst[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
-  }
   Acc acc;
   acc_zero(acc);
   if (!kFirst) {
@@ -765,7 +798,7 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kQL; ++q) {
           const float4 v = *reinterpret_cast<const float4*>(src + min(n0 + acc_col4(wn, ni, q, lane), a.H - 4));
           acc.c[mi][ni][4 * q] = v.x;
           acc.c[mi][ni][4 * q + 1] = v.y;
@@ -775,6 +808,13 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
       // bound the loads in flight (each block lands in its accumulator)
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the reloaded chain values enter the engine in accumulator registers
+    // (left to itself, the register allocator splits the accumulators
+    // between the register files and spills them)
+#pragma unroll
+    for (int mi = 0; mi < kBlocks; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) asm volatile("" : "+a"(acc.c[mi][ni]));
   }
   // (a pass's tile runs past the row tile; rows past dZ's last repeat it)
   const RowsK A = rows_k(a.dZ + (size_t)i0 * a.bg.ldz, min(kBM - 1, a.bg.T_pad - 1 - i0), a.bg.ldz);
@@ -788,14 +828,22 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 #pragma unroll
   for (int i = 0; i < kDma; ++i) B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
   if constexpr (kPart) {
-    static_assert(8 * kDma <= 32 * kBlocks && kWaveRows % (8 * kDma) == 0, "a wave's load rows in one half of its wave row");
+    static_assert(8 * kDma <= kBlk * kBlocks && kWaveRows % (8 * kDma) == 0, "a wave's load rows in one half of its wave row");
     const int wl = __builtin_amdgcn_readfirstlane(w);
-    if ((8 * kDma * wl) % kWaveRows < 32 * kBlocks)  // this wave's load rows hold computed rows
+    if ((8 * kDma * wl) % kWaveRows < kBlk * kBlocks)  // this wave's load rows hold computed rows
       gemm256<false, true, kBlocks, true>(A, B, a.bg.ldz / kBK, acc, lds);
     else
       gemm256<false, true, kBlocks, false>(A, B, a.bg.ldz / kBK, acc, lds);
   } else {
     gemm256<false, true>(A, B, a.bg.ldz / kBK, acc, lds);
+  }
+  // output rows of this lane's active rows: loaded after the vocabulary-long
+  // chain (one load latency per tile; held through the loop they would take
+  // registers the loop needs)
+  int dst[kMI];
+  if (kLast) {
+#pragma unroll
+    for (int mi = 0; mi < kBlocks; ++mi) dst[mi] = a.idx[min(i0 + acc_row(wm, mi, lane), n_act - 1)];
   }
 #pragma unroll
   for (int mi = 0; mi < kBlocks; ++mi) {
@@ -804,10 +852,10 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (n0 + 128 * wn + 32 * ni + 8 * q >= a.H) continue;  // wave-uniform
+      for (int q = 0; q < kQL; ++q) {
+        if (n0 + 128 * wn + kBlk * ni + 4 * kLPR * q >= a.H) continue;  // wave-uniform
         const int n = n0 + acc_col4(wn, ni, q, lane);
-        const f32x16& c = acc.c[mi][ni];
+        const AccBlk& c = acc.c[mi][ni];
         if (kLast)
           *reinterpret_cast<uint2*>(a.grad_h + (size_t)dst[mi] * a.H + n) =
               make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
@@ -860,15 +908,41 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
 
 // ---------------------------------------------------------------------------
 // Benchmark only: the MFMA ceiling of the part under realistic operands.
-// Each wave holds the engine's 128 x 128 fp32 tile (16 blocks of 32 x 32 in
-// accumulator registers) and issues nothing but v_mfma_f32_32x32x16_bf16,
-// cycling through 4 register sets of the caller's random bf16 data so the
-// matrix cores see realistic bit toggling; no memory traffic in the loop.
-// src: 32 * 256 16-byte pieces; out: one float per thread (keeps the result).
+// Each wave holds the engine's 128 x 128 fp32 tile in accumulator registers
+// and issues nothing but the engine's MFMA instruction (64 16 x 16 x 32 or
+// 16 32 x 32 x 16 blocks), cycling through register sets of the caller's
+// random bf16 data so the matrix cores see realistic bit toggling; no
+// memory traffic in the loop.  Either shape does 2^21 FLOP per wave per
+// iteration.  src: 32 * 256 16-byte pieces; out: one float per thread
+// (keeps the result).
 // ---------------------------------------------------------------------------
 #ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ceiling(
     const u32x4* __restrict__ src, float* __restrict__ out, int iters) {
+#if RLK_MFMA == 16
+  bf16x8 fa[2][8], fb[2][8];  // [set][fragment]
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      fa[s][j] = __builtin_bit_cast(bf16x8, src[(s * 16 + j) * 256 + threadIdx.x]);
+      fb[s][j] = __builtin_bit_cast(bf16x8, src[(s * 16 + 8 + j) * 256 + threadIdx.x]);
+    }
+  AccBlk c[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) c[j] = AccBlk{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 64; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[s][j & 7], fa[s][j >> 3], c[j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 64; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t += c[j][i];
+#else
   bf16x8 fa[4][4], fb[4][4];  // [set][fragment]
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -891,6 +965,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int j = 0; j < 16; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) t += c[j][i];
+#endif
   out[blockIdx.x * 256 + threadIdx.x] = t;
 }
 #endif
@@ -923,9 +998,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kQL; ++q) {
         const int j = n0 + acc_col4(wn, ni, q, lane);
-        const f32x16& c = acc.c[mi][ni];
+        const AccBlk& c = acc.c[mi][ni];
         const float v0 = c[4 * q], v1 = c[4 * q + 1], v2 = c[4 * q + 2], v3 = c[4 * q + 3];
         if (a.c_bf16) {
           uint16_t* row = static_cast<uint16_t*>(a.C) + (size_t)i * a.ldc;

@@ -45,7 +45,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_contract_version_and_status_strings():
     L = rlk.lib()
-    assert L.rlk_contract_version() == 1
+    # the default build implements contract 2 (16 x 16 x 32 MFMA steps)
+    assert L.rlk_contract_version() == 2
     for s in range(9):
         assert len(L.rlk_status_string(s)) > 0
     assert L.rlk_status_string(99) == b"unknown status"
