@@ -114,11 +114,27 @@ constexpr int kLdsU4 = kSlots * kTileU4;   // 160 KB, all of a CU's LDS
 // (row >> 1) & 7, so 16 consecutive rows of one k piece cover all banks.
 __device__ __forceinline__ int slot_k(int row, int seg) { return row * kSegs + (seg ^ ((row >> 1) & 7)); }
 
-// MN-mode slot of (k-row, 16-byte piece p of 32): 64-byte blocks of the row
-// xor-ed with (k-row & 7).
-__device__ __forceinline__ int slot_mn(int krow, int p) {
-  return krow * 32 + ((((p >> 2) ^ (krow & 7)) << 2) | (p & 3));
+// MN-mode position of the 16-byte piece p (of 32) within its k-row's 512
+// bytes; an involution in p, so the direct loads use it to pick the piece
+// each lane fetches.  A transposing read (ds_read_b64_tr_b16) serves 32
+// lanes per pass, each k-row contributing 32 contiguous bytes (16 columns):
+//   16 x 16 x 32: the pass reads k-rows 8g + 0..3 and 8g + 8 .. 8g + 11 at
+//     the same columns, so 32-byte units are xor-ed with
+//     (k-row & 3) + 4 ((k-row >> 3) & 1): eight distinct bank ranges;
+//   32 x 32 x 16: the pass reads k-rows 0..3 at two neighbouring 32-byte
+//     column ranges, so 64-byte blocks are xor-ed with (k-row & 7).
+// Both are unchanged by the k-step's row offset (32 or 16 rows).
+__device__ __forceinline__ int mn_pos(int krow, int p) {
+  if constexpr (kBlk == 16) {
+    const int f = (krow & 3) | ((krow >> 1) & 4);
+    return (((p >> 1) ^ f) << 1) | (p & 1);
+  } else {
+    return (((p >> 2) ^ (krow & 7)) << 2) | (p & 3);
+  }
 }
+
+// MN-mode slot of (k-row, 16-byte piece p of 32).
+__device__ __forceinline__ int slot_mn(int krow, int p) { return krow * 32 + mn_pos(krow, p); }
 
 // Position of wave w in the tile's wave grid: row group wave_m (kWaveRows
 // rows each), column group wave_n (128 columns each).
@@ -196,8 +212,7 @@ __device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, 
 // 64 (kDma w + i) .. +64, so lane l of it fills slot s = 64 (kDma w + i) + l and
 // fetches the global piece that the swizzled layout puts there:
 //   K mode : row 8 (kDma w + i) + (l >> 3), piece (l & 7) ^ ((row >> 1) & 7)
-//   MN mode: k-row 2 (kDma w + i) + (l >> 5),
-//            piece ((((l & 31) >> 2) ^ (k-row & 7)) << 2) | (l & 3)
+//   MN mode: k-row 2 (kDma w + i) + (l >> 5), piece mn_pos(k-row, l & 31)
 // (i = 0 .. kDma-1).
 // No registers hold the staged data.
 typedef __attribute__((address_space(3))) void lds_void;
@@ -221,10 +236,7 @@ __device__ __forceinline__ int dma_k_row(int i) { return 8 * kDma * (threadIdx.x
 __device__ __forceinline__ int dma_k_seg(int row) { return (threadIdx.x & 7) ^ ((row >> 1) & 7); }
 // MN-mode k-row and piece of instruction i for this thread
 __device__ __forceinline__ int dma_mn_krow(int i) { return 2 * kDma * (threadIdx.x >> 6) + 2 * i + ((threadIdx.x & 63) >> 5); }
-__device__ __forceinline__ int dma_mn_piece(int krow) {
-  const int l = threadIdx.x & 31;
-  return (((l >> 2) ^ (krow & 7)) << 2) | (l & 3);
-}
+__device__ __forceinline__ int dma_mn_piece(int krow) { return mn_pos(krow, threadIdx.x & 31); }
 // LDS byte address of this wave's first direct-load slot in the tile at
 // LDS byte address t (instruction i then writes 1 KB further per i).
 __device__ __forceinline__ uint32_t dma_wave_base(uint32_t t) {

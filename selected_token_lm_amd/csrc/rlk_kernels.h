@@ -699,20 +699,26 @@ __device__ __forceinline__ ColsMN cols_mn(const uint16_t* m, int c0, int ncol, i
   return L;
 }
 
-// MN-mode loader over the group's vocabulary rows of W: k index kg of the
-// group -> split sc = kg / S_pad, row (c_lo + sc) * S + kg % S_pad (clamped
-// to V - 1; those rows meet dz = 0).  A k-block never straddles two splits
-// (S_pad is a multiple of kBK).
+// MN-mode loader over the group's vocabulary rows of W: k-block kt of the
+// group -> split sc = kt / kbps (kbps = S_pad / kBK k-blocks per split),
+// rows (c_lo + sc) * S + kBK (kt - sc kbps) + 0 .. kBK-1, clamped to V - 1
+// (those rows meet dz = 0).  A k-block never straddles two splits (S_pad is
+// a multiple of kBK).  The split index is (kt * rcp) >> 32 with the
+// reciprocal rcp = ceil(2^32 / kbps) (2^32 when kbps = 1), exact while
+// kt kbps < 2^32 (kt < 32 kbps and kbps < 4096 here), so the main loop
+// divides nothing; each load then costs one clamp and one multiply-add per
+// lane.
 struct WRowsMN {
   const char* base;     // W + first column of the tile
+  uint32_t krow[kDma];  // k-row of piece i
   uint32_t col2[kDma];  // byte offset of piece i's column
-  int H, S, S_pad, c_lo, V;
+  int H, S, kbps, c_lo, V;
+  uint64_t rcp;
   __device__ __forceinline__ void one(int i, int kt, uint32_t m0w) const {
-    const int kg = kt * kBK;
-    const int sc = kg / S_pad;
-    const int r0 = min((c_lo + sc) * S + (kg - sc * S_pad), V - 1);
-    const int r = min((c_lo + sc) * S + (kg - sc * S_pad) + dma_mn_krow(i), V - 1);
-    dma16(base + (size_t)r0 * (2 * H), (uint32_t)((r - r0) * (2 * H)) + col2[i], m0w + 1024u * i);
+    const int sc = (int)(((uint64_t)(uint32_t)kt * rcp) >> 32);
+    const int r0 = min((c_lo + sc) * S + kBK * (kt - sc * kbps), V - 1);
+    const uint32_t last = (uint32_t)(V - 1 - r0);  // rows past it are clamped
+    dma16(base + (size_t)r0 * (2 * H), min(krow[i], last) * (uint32_t)(2 * H) + col2[i], m0w + 1024u * i);
   }
   __device__ __forceinline__ void dma(int kt, uint32_t m0w) const {
 #pragma unroll
@@ -822,11 +828,15 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
   B.base = reinterpret_cast<const char*>(a.W + n0);
   B.H = a.H;
   B.S = a.gm.S;
-  B.S_pad = a.bg.S_pad;
+  B.kbps = a.bg.S_pad / kBK;
+  B.rcp = ((uint64_t(1) << 32) + (uint64_t)B.kbps - 1) / (uint64_t)B.kbps;
   B.c_lo = a.bg.c_lo;
   B.V = a.gm.V;
 #pragma unroll
-  for (int i = 0; i < kDma; ++i) B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
+  for (int i = 0; i < kDma; ++i) {
+    B.col2[i] = 2 * (min(n0 + dma_mn_piece(dma_mn_krow(i)) * 8, a.H - 8) - n0);
+    B.krow[i] = (uint32_t)dma_mn_krow(i);
+  }
   if constexpr (kPart) {
     static_assert(8 * kDma <= kBlk * kBlocks && kWaveRows % (8 * kDma) == 0, "a wave's load rows in one half of its wave row");
     const int wl = __builtin_amdgcn_readfirstlane(w);
