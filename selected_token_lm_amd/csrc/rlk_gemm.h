@@ -156,8 +156,12 @@ __device__ __forceinline__ int wave_n(int w) { return w >> (kWM == 2 ? 1 : 2); }
 //            o[J] + 512 kKStep kk and o2[J] + 512 kKStep kk (k-rows +16 keep
 //            the swizzle, k-rows +4 do not, hence two offsets).
 constexpr int kMaxFrags = kMI > kNI ? kMI : kNI;
+// With 16 x 16 blocks the second read's k-rows (+4) keep the swizzle
+// (mn_pos), so it sits 4 rows = 2048 bytes after the first and needs no
+// offset of its own.
+constexpr bool kMnSecondByImm = kBlk == 16;
 struct FragOffs {
-  uint32_t o[kMaxFrags > kKK ? kMaxFrags : kKK], o2[kMaxFrags];
+  uint32_t o[kMaxFrags > kKK ? kMaxFrags : kKK], o2[kMnSecondByImm ? 1 : kMaxFrags];
 };
 
 template <bool MN>
@@ -181,7 +185,7 @@ __device__ __forceinline__ FragOffs frag_offs(int r0, int lane) {
       const int col = r0 + kBlk * J + 16 * (g & (kG - 1)) + 4 * (s & 3);
       const int p = col >> 3, half = (col >> 2) & 1;
       f.o[J] = 16u * (uint32_t)slot_mn(krow, p) + 8u * half;
-      f.o2[J] = 16u * (uint32_t)slot_mn(krow + 4, p) + 8u * half;
+      if constexpr (!kMnSecondByImm) f.o2[J] = 16u * (uint32_t)slot_mn(krow + 4, p) + 8u * half;
     }
   }
   return f;
@@ -198,7 +202,8 @@ __device__ __forceinline__ bf16x8 frag_at(const u32x4* tile, const FragOffs& f, 
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + f.o[kk] + 128u * kBlk * J));
   } else {
     const lds_bf16x4* p0 = (const lds_bf16x4*)(base + f.o[J] + 512u * kKStep * kk);
-    const lds_bf16x4* p1 = (const lds_bf16x4*)(base + f.o2[J] + 512u * kKStep * kk);
+    const uint32_t o1 = kMnSecondByImm ? f.o[J] + 2048u : f.o2[kMnSecondByImm ? 0 : J];
+    const lds_bf16x4* p1 = (const lds_bf16x4*)(base + o1 + 512u * kKStep * kk);
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p0));
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p1));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
