@@ -814,14 +814,15 @@ __device__ __forceinline__ void gradh_tile(GradHArgs a, int id, int rtiles, int 
       // bound the loads in flight (each block lands in its accumulator)
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the reloaded chain values enter the engine in accumulator registers
-    // (left to itself, the register allocator splits the accumulators
-    // between the register files and spills them)
-#pragma unroll
-    for (int mi = 0; mi < kBlocks; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) asm volatile("" : "+a"(acc.c[mi][ni]));
   }
+  // the accumulators enter the engine in accumulator registers: left to
+  // itself, the register allocator splits reloaded chain values between the
+  // register files and spills them, and with zeroed ones it rotates a block
+  // through vector registers on every k-block (a wait on an MFMA result)
+#pragma unroll
+  for (int mi = 0; mi < kBlocks; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) asm volatile("" : "+a"(acc.c[mi][ni]));
   // (a pass's tile runs past the row tile; rows past dZ's last repeat it)
   const RowsK A = rows_k(a.dZ + (size_t)i0 * a.bg.ldz, min(kBM - 1, a.bg.T_pad - 1 - i0), a.bg.ldz);
   WRowsMN B;
