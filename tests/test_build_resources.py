@@ -19,14 +19,17 @@ from selected_token_lm_amd import build as B
 NOT_CHECKED = {"mfma_ceiling"}  # benchmark helper (include/rlk_bench.h)
 
 
-@pytest.fixture(scope="module")
-def resources():
+# 16: the default engine (contract 2, v_mfma_f32_16x16x32_bf16); 32: the
+# build that still implements contract 1 (v_mfma_f32_32x32x16_bf16)
+@pytest.fixture(scope="module", params=[16, 32], ids=["mfma16", "mfma32"])
+def resources(request):
     if not os.path.exists(B.HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
     out = ""
     for src in B.SOURCES:  # both translation units (four- and eight-wave engine)
-        cmd = [B.HIPCC, *flags, "-DRLK_WAVES=4", "--cuda-device-only", "-c", "-o", os.devnull,
+        cmd = [B.HIPCC, *flags, "-DRLK_WAVES=4", f"-DRLK_MFMA={request.param}", "--cuda-device-only", "-c",
+               "-o", os.devnull,
                "-Rpass-analysis=kernel-resource-usage", "-I", os.path.join(B.ROOT, "include"),
                os.path.join(B.CSRC, src)]
         out += subprocess.run(cmd, capture_output=True, text=True, check=True).stderr
