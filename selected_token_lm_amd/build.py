@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "librlk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # rlk_api.hip: the C ABI and every kernel with the RLK_WAVES-wave engine;
-# rlk_tiles_w8.hip: the forward and dz tile kernels with eight waves.
+# rlk_tiles_w8.hip: the forward, dz and gradient tile kernels with eight waves.
 SOURCES = ["rlk_api.hip", "rlk_tiles_w8.hip"]
 
 FLAGS = [
@@ -41,9 +41,9 @@ FLAGS = [
 def build(verbose: bool = True) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    # RLK_WAVES=8: two waves per SIMD in the main unit's engine too (grad
-    # tiles, the dense product; same results; four is the default and the
-    # faster choice for those kernels on MI355X)
+    # RLK_WAVES=8: two waves per SIMD in the main unit's engine too (the
+    # save-logits forward, the dense product; same results; four is the
+    # default)
     waves = os.environ.get("RLK_WAVES", "4")
     if waves not in ("4", "8"):
         raise ValueError(f"RLK_WAVES must be 4 or 8, not {waves!r}")

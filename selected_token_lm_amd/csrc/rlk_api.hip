@@ -567,12 +567,11 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
     ha.ghacc = ghacc;
     ha.grad_h = static_cast<uint16_t*>(grad_h);
     const bool first = c_lo == 0, last = c_lo + G > last_split;
-    void (*kfn)(rlk::GradHArgs, rlk::GradWArgs) =
-        passes ? (first ? (last ? rlk::grad_tiles<true, true, true> : rlk::grad_tiles<true, false, true>)
-                        : (last ? rlk::grad_tiles<false, true, true> : rlk::grad_tiles<false, false, true>))
-               : (first ? (last ? rlk::grad_tiles<true, true, false> : rlk::grad_tiles<true, false, false>)
-                        : (last ? rlk::grad_tiles<false, true, false> : rlk::grad_tiles<false, false, false>));
-    RLK_LAUNCH_FN("grad_tiles", kfn, dim3((unsigned)(gh_blocks + gw_blocks)), dim3(rlk::kThreads), st, ha, wa);
+    {
+      ProfScope _ps("grad_tiles", st);
+      rlk::launch_grad_tiles_w8(first, last, passes, dim3((unsigned)(gh_blocks + gw_blocks)), st, ha, wa);
+    }
+    RLK_TRY(launched("grad_tiles"));
   }
   return ok();
 }

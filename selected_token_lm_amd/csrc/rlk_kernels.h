@@ -22,9 +22,9 @@
 #include "rlk_gemm.h"
 
 // Which unit builds which kernel: the eight-wave unit (RLK_ENGINE_W8) the
-// plain forward's fwd_tiles instance and dz_tiles; the four-wave unit the
-// other fwd_tiles instances (save-logits, small batches), grad_tiles, the
-// dense product, the row kernels and the merges.
+// plain forward's fwd_tiles instance, dz_tiles and grad_tiles; the
+// four-wave unit the other fwd_tiles instances (save-logits, small
+// batches), the dense product, the row kernels and the merges.
 RLK_ENGINE_BEGIN
 
 // ---------------------------------------------------------------------------
@@ -747,6 +747,11 @@ __device__ __forceinline__ void gradw_tile(GradWArgs a, int id, int n_act, u32x4
   const ColsMN B = cols_mn(a.hA, n0, a.H, a.H);
   Acc acc;
   acc_zero(acc);
+  // the accumulators enter the engine in accumulator registers (see gradh_tile)
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) asm volatile("" : "+a"(acc.c[mi][ni]));
   // no active rows: grad_W is zero
   if (n_act > 0) gemm256<true, true>(A, B, (n_act + kBK - 1) / kBK, acc, lds);
   const int lane = tid & 63, w = tid >> 6, wm = wave_m(w), wn = wave_n(w);

@@ -18,4 +18,10 @@ __attribute__((visibility("hidden"))) void launch_fwd_tiles_w8(dim3 grid, hipStr
 // dz_tiles, eight waves per tile.
 __attribute__((visibility("hidden"))) void launch_dz_tiles_w8(dim3 grid, hipStream_t st, const DzArgs& a);
 
+// grad_tiles<first, last, part>: a backward group's grad_h and grad_W
+// tiles, eight waves per tile.
+__attribute__((visibility("hidden"))) void launch_grad_tiles_w8(bool first, bool last, bool part, dim3 grid,
+                                                               hipStream_t st, const GradHArgs& ha,
+                                                               const GradWArgs& wa);
+
 }  // namespace rlk

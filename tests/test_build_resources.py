@@ -57,8 +57,9 @@ def test_every_operator_kernel_is_reported(resources):
     names = {short(k) for k in resources}
     assert {"fwd_tiles", "dz_tiles", "grad_tiles", "gemm_tiles", "merge_splits", "merge_parts",
             "dz_saved", "compact_rows", "gather_rows"} <= names, names
-    # the eight-wave unit's forward and dz kernels
-    assert {short(k) for k in resources if k.startswith("_ZN3rlk2w8")} == {"fwd_tiles", "dz_tiles"}, names
+    # the eight-wave unit's forward, dz and gradient kernels
+    assert {short(k) for k in resources if k.startswith("_ZN3rlk2w8")} == {"fwd_tiles", "dz_tiles",
+                                                                          "grad_tiles"}, names
 
 
 def test_no_scratch_in_operator_kernels(resources):
