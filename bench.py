@@ -385,16 +385,23 @@ def device_info(torch):
 
 
 def host_cpu():
-    """(CPU model, the cores this process may run on)."""
-    model = None
+    """(CPU model, the cores this process may run on).  The model is cpuinfo's
+    name of the first CPU with its family / model / stepping numbers (a
+    virtual machine may report a bare vendor name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                if not line.strip():
+                    break  # end of the first CPU's record
+                k, _, v = line.partition(":")
+                fields.setdefault(k.strip(), v.strip())
     except OSError:
         pass
+    model = fields.get("model name")
+    nums = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    if model and nums:
+        model = f"{model} ({', '.join(nums)})"
     return model, len(os.sched_getaffinity(0))
 
 
