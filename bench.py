@@ -838,7 +838,8 @@ def main():
                     "2.4 GHz it assumes (clock_power)",
             "tflops": PEAK_BF16 / 1e12 * clock_power["gfx_clock_mhz"]["median"] / 2400.0,
             "dominant_kernel_frac": achieved / (PEAK_BF16 * clock_power["gfx_clock_mhz"]["median"] / 2400.0)},
-        "mfma_ceiling": {"what": "pure loop of the tile engine's MFMA instruction on random bf16 operands, no memory traffic, "
+        "mfma_ceiling": {"what": "pure loop of the tile engine's MFMA instruction on random bf16 operands, eight waves "
+                                 "per compute unit with the tile kernels' 64 x 128 wave tile, no memory traffic, "
                                  "same box after the timed steps (rlk_bench_mfma_ceiling)",
                          "best_tflops": ceiling["best_tflops"], "median_tflops": ceiling["median_tflops"],
                          "dominant_kernel_frac_of_ceiling": achieved / 1e12 / ceiling["median_tflops"]},

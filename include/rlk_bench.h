@@ -18,15 +18,16 @@ extern "C" {
 #endif
 
 /* Benchmark only (computes nothing of the operator): runs `blocks`
- * workgroups of 4 waves, each wave issuing, per iteration, the tile engine's
- * MFMA instruction on a 128 x 128 accumulator tile (128
- * v_mfma_f32_16x16x32_bf16 over 2 register sets of operands; a contract-1
- * build: 64 v_mfma_f32_32x32x16_bf16 over 4 sets), operands of random bf16
- * data, and no memory traffic in the loop: the MFMA throughput the part
- * sustains under its power limit with realistic operand toggling
- * (2^21 FLOP per wave per iteration either way).
- *   src  bf16 device buffer of 32 * 256 * 8 values (random; 16-byte aligned)
- *   out  fp32 [blocks * 256] out (sums of the accumulators, so nothing is
+ * workgroups of 8 waves (two per SIMD, as the eight-wave tile kernels), each
+ * wave issuing, per iteration, the tile engine's MFMA instruction on a
+ * 64 x 128 accumulator tile (64 v_mfma_f32_16x16x32_bf16 over 2 register
+ * sets of operands; a contract-1 build: 32 v_mfma_f32_32x32x16_bf16 over 4
+ * sets), operands of random bf16 data, and no memory traffic in the loop:
+ * the MFMA throughput the part sustains under its power limit with
+ * realistic operand toggling (2^20 FLOP per wave, 2^23 per workgroup, per
+ * iteration either way).
+ *   src  bf16 device buffer of 24 * 512 * 8 values (random; 16-byte aligned)
+ *   out  fp32 [blocks * 512] out (sums of the accumulators, so nothing is
  *        optimised away) */
 rlk_status rlk_bench_mfma_ceiling(const void* src, float* out, int32_t blocks, int32_t iters,
                                   void* stream);

@@ -419,12 +419,13 @@ def rl_token_loss(logp, logp_old, adv, y, eps_low: float = 0.2, eps_high: float 
 def bench_mfma_ceiling(blocks: int = 256, iters: int = 4096, repeats: int = 3):
     """Benchmark only: TFLOP/s of a pure loop of the tile engine's MFMA
     instruction (v_mfma_f32_16x16x32_bf16; v_mfma_f32_32x32x16_bf16 in a
-    contract-1 build) on random operands (no memory traffic), best and median
-    of `repeats` timed launches.  2^21 FLOP per wave per iteration."""
+    contract-1 build) on random operands (no memory traffic), eight waves per
+    workgroup as in the eight-wave tile kernels, best and median of `repeats`
+    timed launches.  2^23 FLOP per workgroup per iteration."""
     gen = torch.Generator(device="cuda").manual_seed(12345)
-    src = torch.randn(32 * 256 * 8, device="cuda", generator=gen).to(torch.bfloat16)
-    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    flops = 2.0 * 32 * 32 * 16 * 64 * iters * 4 * blocks
+    src = torch.randn(24 * 512 * 8, device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    flops = float(2 ** 23) * iters * blocks
     times = []
     for r in range(repeats + 1):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -733,7 +733,7 @@ rlk_status rlk_bench_mfma_ceiling(const void* src, float* out, int32_t blocks, i
   if (!src || !out) return fail(RLK_ERR_NULL_ARG, "src and out are required");
   if (!aligned16(src)) return fail(RLK_ERR_BAD_ALIGNMENT, "src must be 16-byte aligned");
   RLK_TRY(check_device());
-  RLK_LAUNCH(mfma_ceiling, dim3((unsigned)blocks), dim3(256), static_cast<hipStream_t>(stream),
+  RLK_LAUNCH(mfma_ceiling, dim3((unsigned)blocks), dim3(rlk::kCeilThreads), static_cast<hipStream_t>(stream),
              static_cast<const rlk::u32x4*>(src), out, (int)iters);
   return ok();
 }

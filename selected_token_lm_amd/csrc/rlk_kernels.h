@@ -924,65 +924,56 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
 
 // ---------------------------------------------------------------------------
 // Benchmark only: the MFMA ceiling of the part under realistic operands.
-// Each wave holds the engine's 128 x 128 fp32 tile in accumulator registers
-// and issues nothing but the engine's MFMA instruction (64 16 x 16 x 32 or
-// 16 32 x 32 x 16 blocks), cycling through register sets of the caller's
-// random bf16 data so the matrix cores see realistic bit toggling; no
-// memory traffic in the loop.  Either shape does 2^21 FLOP per wave per
-// iteration.  src: 32 * 256 16-byte pieces; out: one float per thread
+// Eight waves per workgroup (two per SIMD), each holding the eight-wave
+// tile kernels' 64 x 128 fp32 wave tile in registers and issuing nothing but
+// the engine's MFMA instruction (32 16 x 16 x 32 or 8 32 x 32 x 16 blocks
+// per operand set), cycling through register sets of the caller's random
+// bf16 data so the matrix cores see realistic bit toggling; no memory
+// traffic in the loop.  (One wave per SIMD cannot issue these MFMAs back to
+// back: such a loop took 1.35-1.47 times the issue cycles, so it would
+// understate the ceiling.)  Either shape does 2^20 FLOP per wave per
+// iteration.  src: 24 * 512 16-byte pieces; out: one float per thread
 // (keeps the result).
 // ---------------------------------------------------------------------------
 #ifndef RLK_ENGINE_W8
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_ceiling(
+constexpr int kCeilThreads = 512;
+__global__ __launch_bounds__(kCeilThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_ceiling(
     const u32x4* __restrict__ src, float* __restrict__ out, int iters) {
 #if RLK_MFMA == 16
-  bf16x8 fa[2][8], fb[2][8];  // [set][fragment]
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      fa[s][j] = __builtin_bit_cast(bf16x8, src[(s * 16 + j) * 256 + threadIdx.x]);
-      fb[s][j] = __builtin_bit_cast(bf16x8, src[(s * 16 + 8 + j) * 256 + threadIdx.x]);
-    }
-  AccBlk c[64];
-#pragma unroll
-  for (int j = 0; j < 64; ++j) c[j] = AccBlk{};
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int j = 0; j < 64; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[s][j & 7], fa[s][j >> 3], c[j], 0, 0, 0);
-  }
-  float t = 0.f;
-#pragma unroll
-  for (int j = 0; j < 64; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t += c[j][i];
+  constexpr int kS = 2, kA = 4, kB = 8;  // operand sets; A and B fragments per set (4 x 8 blocks)
 #else
-  bf16x8 fa[4][4], fb[4][4];  // [set][fragment]
+  constexpr int kS = 4, kA = 2, kB = 4;  // 2 x 4 blocks of 32 x 32
+#endif
+  bf16x8 fa[kS][kA], fb[kS][kB];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < kS; ++s) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      fa[s][j] = __builtin_bit_cast(bf16x8, src[(s * 8 + j) * 256 + threadIdx.x]);
-      fb[s][j] = __builtin_bit_cast(bf16x8, src[(s * 8 + 4 + j) * 256 + threadIdx.x]);
-    }
-  f32x16 c[16];
+    for (int j = 0; j < kA; ++j)
+      fa[s][j] = __builtin_bit_cast(bf16x8, src[(s * (kA + kB) + j) * kCeilThreads + threadIdx.x]);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) c[j] = f32x16{};
+    for (int j = 0; j < kB; ++j)
+      fb[s][j] = __builtin_bit_cast(bf16x8, src[(s * (kA + kB) + kA + j) * kCeilThreads + threadIdx.x]);
+  }
+  AccBlk c[kA * kB];
+#pragma unroll
+  for (int j = 0; j < kA * kB; ++j) c[j] = AccBlk{};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < kS; ++s)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j & 3], fa[s][j >> 2], c[j], 0, 0, 0);
+      for (int j = 0; j < kA * kB; ++j)
+#if RLK_MFMA == 16
+        c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[s][j % kB], fa[s][j / kB], c[j], 0, 0, 0);
+#else
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j % kB], fa[s][j / kB], c[j], 0, 0, 0);
+#endif
   }
   float t = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < kA * kB; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t += c[j][i];
-#endif
-  out[blockIdx.x * 256 + threadIdx.x] = t;
+    for (int i = 0; i < kBlk * kBlk / 64; ++i) t += c[j][i];
+  out[blockIdx.x * kCeilThreads + threadIdx.x] = t;
 }
 #endif
 
