@@ -929,9 +929,7 @@ __global__ __launch_bounds__(256) void rl_token_loss(RlLossArgs a) {
 // the engine's MFMA instruction (32 16 x 16 x 32 or 8 32 x 32 x 16 blocks
 // per operand set), cycling through register sets of the caller's random
 // bf16 data so the matrix cores see realistic bit toggling; no memory
-// traffic in the loop.  (One wave per SIMD cannot issue these MFMAs back to
-// back: such a loop took 1.35-1.47 times the issue cycles, so it would
-// understate the ceiling.)  Either shape does 2^20 FLOP per wave per
+// traffic in the loop.  Either shape does 2^20 FLOP per wave per
 // iteration.  src: 24 * 512 16-byte pieces; out: one float per thread
 // (keeps the result).
 // ---------------------------------------------------------------------------
