@@ -338,8 +338,9 @@ def clock_power_window(torch, step, seconds=2.5, settle=0.75):
     return res
 
 
-def rocminfo_name(arch="gfx950"):
-    """Marketing name of the first `arch` agent that rocminfo lists, or None."""
+def rocminfo_agent(arch="gfx950"):
+    """The first `arch` agent that rocminfo lists: its name, marketing name
+    (empty on some systems), chip id and compute units; None without rocminfo."""
     import subprocess
     try:
         txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
@@ -352,7 +353,8 @@ def rocminfo_name(arch="gfx950"):
                 k, v = line.split(":", 1)
                 fields.setdefault(k.strip(), v.strip())
         if fields.get("Name", "").startswith(arch):
-            return fields.get("Marketing Name")
+            return {"name": fields.get("Name"), "marketing_name": fields.get("Marketing Name"),
+                    "chip_id": fields.get("Chip ID"), "compute_units": fields.get("Compute Unit")}
     return None
 
 
@@ -379,7 +381,7 @@ def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     market, product = amdsmi_names(torch)
     # the clock and power under load come from ClockPowerSampler
-    return {"name": p.name, "rocminfo_marketing_name": rocminfo_name(), "amdsmi_market_name": market,
+    return {"name": p.name, "rocminfo": rocminfo_agent(), "amdsmi_market_name": market,
             "amdsmi_product_name": product, "arch": getattr(p, "gcnArchName", ""),
             "compute_units": p.multi_processor_count}
 
