@@ -264,3 +264,15 @@ def test_fused_rl_forward_validation():
     assert call(H=96) == BAD_SHAPE
     assert call(nbytes=10) == WS_SMALL
     assert call(T=0, old=None, adv=None, logp=None, loss=None, g=None) == OK
+
+
+def test_mfma_ceiling_validation():
+    # the benchmark helper checks its arguments before any device call
+    L = rlk.lib()
+    f = L.rlk_bench_mfma_ceiling
+    assert f(FAKE, FAKE, 0, 10, None) == BAD_ARG
+    assert f(FAKE, FAKE, 65537, 10, None) == BAD_ARG
+    assert f(FAKE, FAKE, 256, 0, None) == BAD_ARG
+    assert f(None, FAKE, 256, 10, None) == NULL_ARG
+    assert f(FAKE, None, 256, 10, None) == NULL_ARG
+    assert f(MISALIGNED, FAKE, 256, 10, None) == BAD_ALIGN
