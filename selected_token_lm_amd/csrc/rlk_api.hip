@@ -182,10 +182,13 @@ bool grad_h_passes(int64_t row_tiles, int64_t n_tiles) {
   return 3 * row_tiles * n_tiles <= device_cus();
 }
 
-// Grids stay within HIP's limit of 2^32 - 1 threads per launch dimension
-// (checked for the larger of the two block sizes).
+// Tile grids stay within the 2^31 - 1 threads a launch holds along x
+// (checked for the larger of the two block sizes).  Row-wise kernels take
+// at most kRowBlocks blocks and stride over the rows.
+constexpr int64_t kRowBlocks = int64_t(1) << 22;  // 256-thread blocks: 2^30 threads
+constexpr int64_t kRowBlocksY = 65535;            // the limit along y
 rlk_status check_grid(int64_t blocks) {
-  if (blocks * std::max(rlk::kThreads, rlk::kThreadsW8) > (int64_t)UINT32_MAX)
+  if (blocks * std::max(rlk::kThreads, rlk::kThreadsW8) > (int64_t)INT32_MAX)
     return fail(RLK_ERR_BAD_SHAPE, "problem needs %lld tile blocks, more than one launch holds", (long long)blocks);
   return RLK_OK;
 }
@@ -333,8 +336,9 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, yA, n_act,
              mode == 0 ? logp : nullptr, mode == 0 ? lse : nullptr, mode == 1 ? pr : nullptr,
              rl ? rl->loss : nullptr, rl ? rl->g : nullptr);
-  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, static_cast<const uint16_t*>(h), idx, n_act,
-             (int)H, (int)V_global, y, nullptr, nullptr, hA, nullptr);
+  RLK_LAUNCH(gather_rows, dim3((unsigned)std::min(L.T_pad, kRowBlocks)), dim3(256), st,
+             static_cast<const uint16_t*>(h), idx, n_act, (int)L.T_pad, (int)H, (int)V_global, y, nullptr, nullptr, hA,
+             nullptr);
 
   rlk::SplitGeom gm;
   gm.V = (int)g.V;
@@ -496,10 +500,11 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
 
   RLK_LAUNCH(compact_rows, dim3(1), dim3(1024), st, y, (int)T, ignore_index, idx, nullptr, n_act, nullptr, nullptr,
              nullptr, nullptr, nullptr);
-  RLK_LAUNCH(gather_rows, dim3((unsigned)L.T_pad), dim3(256), st, hb, idx, n_act, (int)H, (int)V, y, lse, g, hA,
-             rowinfo);
+  RLK_LAUNCH(gather_rows, dim3((unsigned)std::min(L.T_pad, kRowBlocks)), dim3(256), st, hb, idx, n_act, (int)L.T_pad,
+             (int)H, (int)V, y, lse, g, hA, rowinfo);
   if (grad_h) {
-    RLK_LAUNCH(zero_rows, dim3((unsigned)T), dim3(256), st, y, ignore_index, (int)H, static_cast<uint16_t*>(grad_h));
+    RLK_LAUNCH(zero_rows, dim3((unsigned)std::min(T, kRowBlocks)), dim3(256), st, y, (int)T, ignore_index, (int)H,
+               static_cast<uint16_t*>(grad_h));
   }
   rlk::SplitGeom gm;
   gm.V = (int)gg.V;
@@ -540,8 +545,8 @@ rlk_status run_backward(const void* h, const void* W, const int32_t* y, const fl
     da.bg = bg;
     da.dZ = dZ;
     if (zsave)
-      RLK_LAUNCH(dz_saved, dim3((unsigned)ceil_div(bg.ldz / 8, 256), (unsigned)L.T_pad), dim3(256), st, zsave, ldzs,
-                 idx, rowinfo, n_act, gm, bg, dZ);
+      RLK_LAUNCH(dz_saved, dim3((unsigned)ceil_div(bg.ldz / 8, 256), (unsigned)std::min(L.T_pad, kRowBlocksY)),
+                 dim3(256), st, zsave, ldzs, idx, rowinfo, n_act, gm, bg, dZ);
     else
       RLK_LAUNCH_W8("dz_tiles", launch_dz_tiles_w8, dim3((unsigned)dz_blocks), st, da);
 

@@ -624,46 +624,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // layout as dZ) instead of a recomputed tile: the same z bits, primitives
 // and rounding as dz_tiles, so the same dz bits.  One thread per 8
 // consecutive dZ columns of one compacted row; grid (G * S_pad / 8 / 256,
-// T_pad); rows past the active row tiles are left alone (never read).
+// min(T_pad, 65535)), rows blockIdx.y, + gridDim.y, ... (grid.y holds at
+// most 65535); rows past the active row tiles are left alone (never read).
 #ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void dz_saved(const float* __restrict__ zsave, int64_t ldzs,
                                                  const int32_t* __restrict__ idx, const float4* __restrict__ rowinfo,
                                                  const int32_t* __restrict__ n_act_p, SplitGeom gm, BwdGeom bg,
                                                  uint16_t* __restrict__ dZ) {
-  const int i = blockIdx.y;
   const int col0 = 8 * (blockIdx.x * 256 + threadIdx.x);  // column within the group's dZ row
   if (col0 >= bg.ldz) return;
   const int n_act = *n_act_p;
-  if (i >= ((n_act + kBM - 1) / kBM) * kBM) return;
+  const int rows = ((n_act + kBM - 1) / kBM) * kBM;
   const int sc = col0 / bg.S_pad, vl0 = col0 - sc * bg.S_pad;
   const int sbeg = (bg.c_lo + sc) * gm.S;
   const int valid_s = max(0, min(gm.S, gm.V - sbeg));
-  float d[8];
-  if (i < n_act) {
-    const float4 ri = rowinfo[i];
-    const float L = ri.x, gi = ri.y;
-    const int yl = __float_as_int(ri.z) - sbeg;
-    // 16-byte aligned: ldzs, S_pad and col0 are multiples of 4
-    const float4* zr = reinterpret_cast<const float4*>(zsave + (size_t)idx[i] * ldzs + (size_t)bg.c_lo * bg.S_pad + col0);
-    const float4 z0 = zr[0], z1 = zr[1];
-    const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+  for (int i = blockIdx.y; i < rows; i += gridDim.y) {
+    float d[8];
+    if (i < n_act) {
+      const float4 ri = rowinfo[i];
+      const float L = ri.x, gi = ri.y;
+      const int yl = __float_as_int(ri.z) - sbeg;
+      // 16-byte aligned: ldzs, S_pad and col0 are multiples of 4
+      const float4* zr = reinterpret_cast<const float4*>(zsave + (size_t)idx[i] * ldzs + (size_t)bg.c_lo * bg.S_pad + col0);
+      const float4 z0 = zr[0], z1 = zr[1];
+      const float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int vl = vl0 + e;
-      if (vl < valid_s) {
-        const float p = rlk_exp(z[e] - L);
-        const float delta = (vl == yl) ? 1.f : 0.f;
-        d[e] = gi * (delta - p);
-      } else {
-        d[e] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const int vl = vl0 + e;
+        if (vl < valid_s) {
+          const float p = rlk_exp(z[e] - L);
+          const float delta = (vl == yl) ? 1.f : 0.f;
+          d[e] = gi * (delta - p);
+        } else {
+          d[e] = 0.f;
+        }
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.f;
+      for (int e = 0; e < 8; ++e) d[e] = 0.f;
+    }
+    *reinterpret_cast<u32x4*>(dZ + (size_t)i * bg.ldz + col0) =
+        u32x4{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])};
   }
-  *reinterpret_cast<u32x4*>(dZ + (size_t)i * bg.ldz + col0) =
-      u32x4{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])};
 }
 #endif
 
@@ -1042,36 +1044,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // term.  grid rows, block 256; 16-byte pieces.
 #ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
-                                                   const int32_t* __restrict__ n_act_p, int H, int V,
+                                                   const int32_t* __restrict__ n_act_p, int rows, int H, int V,
                                                    const int32_t* __restrict__ y, const float* __restrict__ lse,
                                                    const float* __restrict__ g, uint16_t* __restrict__ hA,
                                                    float4* __restrict__ rowinfo) {
-  const int i = blockIdx.x;
   const int n_act = *n_act_p;
-  u32x4* dst = reinterpret_cast<u32x4*>(hA + (size_t)i * H);
-  if (i < n_act) {
-    const int t = idx[i];
-    const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)t * H);
-    for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
-    if (rowinfo && threadIdx.x == 0) {
-      const int yt = y[t];
-      const float gt = (yt >= 0 && yt < V) ? g[t] : __builtin_nanf("");
-      rowinfo[i] = make_float4(lse[t], gt, __int_as_float(yt), 0.f);
+  // rows blockIdx.x, + gridDim.x, ... (a launch holds at most 2^31 - 1
+  // threads along x, so the grid may be smaller than `rows`)
+  for (int i = blockIdx.x; i < rows; i += gridDim.x) {
+    u32x4* dst = reinterpret_cast<u32x4*>(hA + (size_t)i * H);
+    if (i < n_act) {
+      const int t = idx[i];
+      const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)t * H);
+      for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = src[p];
+      if (rowinfo && threadIdx.x == 0) {
+        const int yt = y[t];
+        const float gt = (yt >= 0 && yt < V) ? g[t] : __builtin_nanf("");
+        rowinfo[i] = make_float4(lse[t], gt, __int_as_float(yt), 0.f);
+      }
+    } else {
+      for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
+      if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
     }
-  } else {
-    for (int p = threadIdx.x; p < H / 8; p += 256) dst[p] = u32x4{0u, 0u, 0u, 0u};
-    if (rowinfo && threadIdx.x == 0) rowinfo[i] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
   }
 }
 #endif
 
 // Zero the grad_h rows of inactive rows.  grid T, block 256.
 #ifndef RLK_ENGINE_W8
-__global__ __launch_bounds__(256) void zero_rows(const int32_t* __restrict__ y, int ignore_index, int H,
+__global__ __launch_bounds__(256) void zero_rows(const int32_t* __restrict__ y, int T, int ignore_index, int H,
                                                  uint16_t* __restrict__ grad_h) {
-  const int t = blockIdx.x;
-  if (y[t] != ignore_index) return;
-  for (int k = threadIdx.x; k < H; k += 256) grad_h[(size_t)t * H + k] = 0;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {  // (as in gather_rows)
+    if (y[t] != ignore_index) continue;
+    for (int k = threadIdx.x; k < H; k += 256) grad_h[(size_t)t * H + k] = 0;
+  }
 }
 #endif
 
