@@ -357,32 +357,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 }
 
 // ---------------------------------------------------------------------------
-// Split fold + tree + epilogue.  grid.x: 64 active rows per block; 16 waves,
-// wave w folds splits w, w+16 of the range (chunks left to right), the
-// split statistics meet in LDS and one thread per row runs the pairwise
-// tree over the nsplit splits.
+// Split fold + tree + epilogue.  grid.x: kMergeRows rows per block; thread
+// (split s, row r) folds split s of the range for row r (chunks left to
+// right), the split statistics meet in LDS and one thread per row runs the
+// pairwise tree over the nsplit splits.
 // mode 0 (forward):  logp[t] = (z_t - m) - log s, lse[t] = m + log s, and
 //                    when rl.loss or rl.g is set the per-token RL objective
 //                    of that logp (rl_token: the same bits as rl_token_loss)
 // mode 1 (partial):  pout[t] = {m, s, owned ? z_t : 0, owned}
 // ---------------------------------------------------------------------------
-constexpr int kMergeWaves = 16;  // waves of merge_splits (64 rows per block)
+constexpr int kMergeRows = 16;  // rows per block of merge_splits (one thread per row and split)
 #ifndef RLK_ENGINE_W8
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* __restrict__ rec, size_t rec_stride,
+__global__ __launch_bounds__(kMergeRows * kNSplit) void merge_splits(const float2* __restrict__ rec, size_t rec_stride,
                                                     const float* __restrict__ zt, const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ n_act_p,
                                                     const int32_t* __restrict__ y, SplitGeom gm, int nsplit, int mode,
                                                     int own_lo, int own_hi, float* __restrict__ logp,
                                                     float* __restrict__ lse, PartialRec* __restrict__ pout,
                                                     RlLossArgs rl) {
-  __shared__ MS red[kNSplit][64];
+  __shared__ MS red[kNSplit][kMergeRows];
   const int n_act = *n_act_p;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = blockIdx.x * 64 + lane;
-  if (blockIdx.x * 64 >= n_act) return;
-  for (int sl = wave; sl < nsplit; sl += kMergeWaves) {
+  const int lane = threadIdx.x % kMergeRows, sl = threadIdx.x / kMergeRows;
+  const int i = blockIdx.x * kMergeRows + lane;
+  if (blockIdx.x * kMergeRows >= n_act) return;
+  {
     MS r = ms_identity();
-    if (i < n_act) {
+    if (sl < nsplit && i < n_act) {
       // chunks of the split that hold vocabulary columns (the others carry
       // no record); their records are loaded kBatch at a time ahead of the
       // fold, which still takes them left to right
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_splits(const float2* _
     red[sl][lane] = r;
   }
   __syncthreads();
-  if (wave != 0 || i >= n_act) return;
+  if (sl != 0 || i >= n_act) return;
   MS v[kNSplit];
 #pragma unroll
   for (int s = 0; s < kNSplit; ++s) v[s] = (s < nsplit) ? red[s][lane] : ms_identity();
