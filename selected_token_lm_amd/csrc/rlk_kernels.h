@@ -76,26 +76,48 @@ __global__ __launch_bounds__(1024) void compact_rows(const int32_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) base_s = 0;
   __syncthreads();
-  for (int t0 = 0; t0 < T; t0 += 1024) {
-    const int t = t0 + tid;
-    const int yt = (t < T) ? y[t] : ignore_index;
-    const bool act = yt != ignore_index;
-    if (t < T && !act) {
-      if (logp) logp[t] = 0.f;
-      if (lse) lse[t] = 0.f;
-      if (pout) pout[t] = PartialRec{-INFINITY, 0.f, 0.f, 0u};
-      if (rl_loss) rl_loss[t] = 0.f;
-      if (rl_g) rl_g[t] = 0.f;
+  // a pass covers 1024 kPer rows, thread tid rows t0 + kPer tid .. + kPer - 1
+  // (ascending), so the block-wide exclusive scan of the per-thread counts
+  // gives every active row its place in row order
+  constexpr int kPer = 4;
+  for (int t0 = 0; t0 < T; t0 += 1024 * kPer) {
+    int ys[kPer];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int t = t0 + kPer * tid + e;
+      ys[e] = (t < T) ? y[t] : ignore_index;
+      cnt += ys[e] != ignore_index;
     }
-    const uint64_t bal = __ballot(act);
-    const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    if (lane == 0) wave_tot[wave] = __popcll(bal);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int t = t0 + kPer * tid + e;
+      if (t < T && ys[e] == ignore_index) {
+        if (logp) logp[t] = 0.f;
+        if (lse) lse[t] = 0.f;
+        if (pout) pout[t] = PartialRec{-INFINITY, 0.f, 0.f, 0u};
+        if (rl_loss) rl_loss[t] = 0.f;
+        if (rl_g) rl_g[t] = 0.f;
+      }
+    }
+    // inclusive scan of the counts over the wave
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    int off = base_s;
-    for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (act) {
-      idx[off + before] = t;
-      if (yA) yA[off + before] = yt;
+    int pos = base_s + incl - cnt;
+    for (int w = 0; w < wave; ++w) pos += wave_tot[w];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (ys[e] != ignore_index) {
+        idx[pos] = t0 + kPer * tid + e;
+        if (yA) yA[pos] = ys[e];
+        ++pos;
+      }
     }
     __syncthreads();
     if (tid == 0) {
@@ -1041,7 +1063,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RLK_WA
 // defined log-probability (the forward wrote NaN for it): its g becomes NaN,
 // so that the backward's gradients show it (NaN in the row's grad_h and in
 // every grad_W element it reaches) instead of silently dropping the target
-// term.  grid rows, block 256; 16-byte pieces.
+// term.  Block 256, 16-byte pieces.
 #ifndef RLK_ENGINE_W8
 __global__ __launch_bounds__(256) void gather_rows(const uint16_t* __restrict__ h, const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ n_act_p, int rows, int H, int V,
