@@ -379,8 +379,9 @@ rlk_status run_forward(const void* h, const void* W, const int32_t* y, int64_t T
 
   rlk::RlLossArgs rla{};  // no fused objective unless rl is given
   if (rl) rla = *rl;
-  RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, rlk::kMergeRows)), dim3(rlk::kMergeRows * rlk::kNSplit), st, rec, (size_t)T, zt, idx, n_act, y, gm,
-             nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse, pr, rla);
+  RLK_LAUNCH(merge_splits, dim3((unsigned)ceil_div(T, rlk::kMergeRows)), dim3(rlk::kMergeRows * rlk::kNSplit), st, rec,
+             (size_t)T, zt, idx, n_act, y, gm, nsplit, mode, (int)vocab_start, (int)(vocab_start + vocab_len), logp, lse,
+             pr, rla);
   return RLK_OK;
 }
 
